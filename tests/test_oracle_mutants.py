@@ -1,0 +1,117 @@
+"""Mistakes planted in a copy of the oracle must be caught by its pins.
+
+Each mutant is a small textual edit of oracle/focus_oracle.py (a dropped
+term, a wrong axis, sign, index or offset). The edited source is executed
+into a fresh module on the CPU, swapped in for the oracle's functions, and
+at least one pin of tests/test_oracle_pins.py must then fail. The real
+oracle is never modified.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle
+from oracle import focus_oracle
+from tests import test_oracle_pins as P
+
+PINS = [
+    lambda: P.test_golden_block_attention_importance("importance_gqa_tiny.json"),
+    lambda: P.test_golden_block_attention_importance("scale_d4.json"),
+    P.test_golden_delta_topk_compact,
+    P.test_golden_retained,
+    lambda: P.test_column_sums_equal_block_size(7, 4, 2, 16, [0, 5, 13]),
+    P.test_zero_queries_closed_form,
+    P.test_dominant_key_takes_all_weight,
+    lambda: P.test_attention_matches_torch_sdpa(5, 8, 2, 32, [0, 7, 19]),
+    P.test_importance_brute_force_loops,
+    P.test_permutations,
+    lambda: P.test_maxpool_matches_torch(3),
+    P.test_delta_of_identical_layers_is_zero_and_keeps_first_positions,
+    P.test_topk_matches_torch_and_invariants,
+    P.test_compact_matches_nonzero_and_cumsum,
+    P.test_retained_with_full_budget_equals_block_attention,
+    P.test_retained_matches_torch_sdpa_on_gathered_rows,
+]
+
+# (name, [(old, new, occurrence)])
+MUTANTS = [
+    ("scale dropped", [("return 1.0 / math.sqrt(d)", "return 1.0", 0)]),
+    ("scale 1/d", [("return 1.0 / math.sqrt(d)", "return 1.0 / d", 0)]),
+    ("softmax over queries", [
+        ("m = s.max(axis=1, keepdims=True)", "m = s.max(axis=0, keepdims=True)", 0),
+        ("l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)", 0)]),
+    ("lse without max", [("lse = m[:, 0] + np.log(l[:, 0])",
+                          "lse = np.log(l[:, 0])", 0)]),
+    ("values replaced by keys", [("return p, p @ v, lse", "return p, p @ k, lse", 0)]),
+    ("GQA map h % Hkv in S1", [("g = h // grp", "g = h % hkv", 0)]),
+    ("GQA map h % Hkv in S5", [("g = h // grp", "g = h % hkv", 1)]),
+    ("prefix columns taken as block", [("imp[b, h] = colsum[plen:]",
+                                        "imp[b, h] = colsum[:block]", 0)]),
+    ("prefix offset ignored in S1", [("p0, p1 = int(cu[b]), int(cu[b + 1])",
+                                      "p0, p1 = 0, int(cu[b + 1]) - int(cu[b])", 0)]),
+    ("heads summed", [("mean = np.asarray(imp, dtype=F64).mean(axis=1)",
+                       "mean = np.asarray(imp, dtype=F64).sum(axis=1)", 0)]),
+    ("pool radius k-1", [("r = (pool_k - 1) // 2", "r = pool_k - 1", 0)]),
+    ("pool window short on the right", [
+        ("lo, hi = max(0, j - r), min(blk, j + r + 1)",
+         "lo, hi = max(0, j - r), min(blk, j + r)", 0)]),
+    ("delta sign", [(
+        "return head_mean_maxpool(imp1, pool_k) - head_mean_maxpool(imp0, pool_k)",
+        "return head_mean_maxpool(imp0, pool_k) - head_mean_maxpool(imp1, pool_k)", 0)]),
+    ("ties to higher index", [("key=lambda j: (-d_imp[b, j], j)",
+                               "key=lambda j: (-d_imp[b, j], -j)", 0)]),
+    ("smallest kept", [("key=lambda j: (-d_imp[b, j], j)",
+                        "key=lambda j: (d_imp[b, j], j)", 0)]),
+    ("budget off by one", [("kb = min(max(int(k_keep[b]), 0), blk)",
+                            "kb = min(max(int(k_keep[b]) - 1, 0), blk)", 0)]),
+    ("idx without sequence offset", [("idx.append(b * blk + j)", "idx.append(j)", 0)]),
+    ("cu_ret inclusive", [("cu = [0]", "cu = []", 0)]),
+    ("retained sees every block key", [
+        ("np.asarray(k_src[rows, g], F64)",
+         "np.asarray(k_src[b * block:(b + 1) * block, g], F64)", 0),
+        ("np.asarray(v_src[rows, g], F64)",
+         "np.asarray(v_src[b * block:(b + 1) * block, g], F64)", 0)]),
+    ("retained prefix from token 0", [("p0, p1 = int(cu_p[b]), int(cu_p[b + 1])",
+                                       "p0, p1 = 0, int(cu_p[b + 1])", 0)]),
+]
+
+EXPORTED = ["attention_rows", "block_attn_importance", "block_step", "compact",
+            "default_scale", "head_mean_maxpool", "importance_delta",
+            "retained_attn", "topk_keep"]
+
+
+def _replace_nth(src, old, new, n):
+    pos = -1
+    for _ in range(n + 1):
+        pos = src.find(old, pos + 1)
+        assert pos >= 0, f"mutation anchor not found: {old!r} #{n}"
+    return src[:pos] + new + src[pos + len(old):]
+
+
+def _mutant_module(edits):
+    src = inspect.getsource(focus_oracle)
+    for old, new, n in edits:
+        src = _replace_nth(src, old, new, n)
+    mod = types.ModuleType("focus_oracle_mutant")
+    exec(compile(src, "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in PINS:
+        pin()
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, edits, monkeypatch):
+    mod = _mutant_module(edits)
+    for fn in EXPORTED:
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    caught = []
+    for i, pin in enumerate(PINS):
+        try:
+            pin()
+        except Exception as exc:  # a failed assertion or a shape error
+            caught.append((i, type(exc).__name__))
+    assert caught, f"no pin caught mutant {name!r}"
