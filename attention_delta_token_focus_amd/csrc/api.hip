@@ -1,0 +1,292 @@
+// C ABI of libfocus: argument validation, launch geometry, error strings.
+// Every entry point checks its host-visible arguments before enqueuing any
+// work and never lets a C++ exception escape.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "focus.h"
+#include "focus_internal.hpp"
+
+namespace {
+
+thread_local std::string tl_error;
+
+focus_status fail(focus_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  tl_error = buf;
+  return s;
+}
+
+focus_status ok() {
+  tl_error.clear();
+  return FOCUS_OK;
+}
+
+focus_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FOCUS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+#define REQUIRE_PTR(p)                                                       \
+  do {                                                                       \
+    if ((p) == nullptr)                                                      \
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);          \
+    if (!aligned16(p))                                                       \
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, \
+                  #p);                                                       \
+  } while (0)
+
+#define OPTIONAL_PTR(p)                                                      \
+  do {                                                                       \
+    if ((p) != nullptr && !aligned16(p))                                     \
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, \
+                  #p);                                                       \
+  } while (0)
+
+focus_status check_attn_shape(const char* fn, int dt, int batch, int B,
+                              int Hq, int Hkv, int d, int max_prefix) {
+  if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+  if (B < 1 || B > 128)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
+  if (Hq < 1 || Hkv < 1)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d / Hkv %d < 1", fn, Hq, Hkv);
+  if (max_prefix < 0)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: max_prefix %d < 0", fn, max_prefix);
+  if (Hq % Hkv != 0)
+    return fail(FOCUS_ERR_UNSUPPORTED, "%s: Hq %d is not a multiple of Hkv %d",
+                fn, Hq, Hkv);
+  if (d != 64 && d != 128)
+    return fail(FOCUS_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, d);
+  if (dt != FOCUS_F32 && dt != FOCUS_BF16)
+    return fail(FOCUS_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dt);
+  return FOCUS_OK;
+}
+
+// Query heads stacked per workgroup: up to 128 rows of rph rows each.
+void head_chunks(int G, int rph, int* hpw, int* n_hc) {
+  int per = focus::kRowsPerWG / rph;
+  if (per < 1) per = 1;
+  if (per > G) per = G;
+  *hpw = per;
+  *n_hc = (G + per - 1) / per;
+}
+
+float log2_scale(float scale, int d) {
+  const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  return s * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* focus_version(void) { return "libfocus 0.1.0 gfx950"; }
+
+const char* focus_status_string(focus_status s) {
+  switch (s) {
+    case FOCUS_OK: return "FOCUS_OK";
+    case FOCUS_ERR_INVALID_ARG: return "FOCUS_ERR_INVALID_ARG";
+    case FOCUS_ERR_UNSUPPORTED: return "FOCUS_ERR_UNSUPPORTED";
+    case FOCUS_ERR_WORKSPACE: return "FOCUS_ERR_WORKSPACE";
+    case FOCUS_ERR_HIP: return "FOCUS_ERR_HIP";
+  }
+  return "FOCUS_ERR_UNKNOWN";
+}
+
+const char* focus_last_error(void) { return tl_error.c_str(); }
+
+focus_status focus_block_attn_importance_workspace(int batch, int B, int Hq,
+                                                   int Hkv, int d,
+                                                   int max_prefix,
+                                                   size_t* bytes) {
+  const char* fn = "focus_block_attn_importance_workspace";
+  if (bytes == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  focus_status st = check_attn_shape(fn, FOCUS_BF16, batch, B, Hq, Hkv, d, max_prefix);
+  if (st != FOCUS_OK) return st;
+  *bytes = 0;
+  return ok();
+}
+
+focus_status focus_block_attn_importance(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
+    const void* v_cache, const int32_t* cu_prefix, int max_prefix, void* out,
+    float* imp, float* lse, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* fn = "focus_block_attn_importance";
+  try {
+    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
+    if (st != FOCUS_OK) return st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k_blk);
+    REQUIRE_PTR(v_blk);
+    REQUIRE_PTR(cu_prefix);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(imp);
+    OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(workspace);
+    if (max_prefix > 0) {
+      REQUIRE_PTR(k_cache);
+      REQUIRE_PTR(v_cache);
+    }
+    size_t need = 0;
+    st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);
+    if (st != FOCUS_OK) return st;
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
+                  fn, workspace_bytes, need);
+    focus::AttnArgs a = {};
+    a.q = q;
+    a.k_blk = k_blk;
+    a.v_blk = v_blk;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cu_prefix = cu_prefix;
+    a.out = out;
+    a.imp = imp;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.rph = B;
+    head_chunks(a.G, B, &a.hpw, &a.n_hc);
+    a.sl2 = log2_scale(scale, d);
+    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    return hip_status(focus::launch_block_attn(e, d, batch, a, (hipStream_t)stream),
+                      "block attention launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status focus_delta_topk(int batch, int B, int Hq, int pool_k,
+                              const float* imp0, const float* imp1,
+                              const int32_t* k_keep, uint8_t* keep, float* dI,
+                              void* stream) {
+  const char* fn = "focus_delta_topk";
+  try {
+    if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+    if (B < 1 || B > 128)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
+    if (Hq < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d < 1", fn, Hq);
+    if (pool_k < 1 || pool_k > 255 || pool_k % 2 == 0)
+      return fail(FOCUS_ERR_UNSUPPORTED, "%s: pool_k %d must be odd in [1, 255]",
+                  fn, pool_k);
+    REQUIRE_PTR(imp0);
+    REQUIRE_PTR(imp1);
+    if (k_keep == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: k_keep is NULL", fn);
+    if (keep == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: keep is NULL", fn);
+    return hip_status(focus::launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1,
+                                               k_keep, keep, dI, (hipStream_t)stream),
+                      "delta/top-K launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status focus_compact(int batch, int B, const uint8_t* keep, int32_t* idx,
+                           int32_t* cu_ret, void* stream) {
+  const char* fn = "focus_compact";
+  try {
+    if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+    if (B < 1 || B > 128)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
+    if (keep == nullptr || idx == nullptr || cu_ret == nullptr)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: keep, idx and cu_ret must be non-NULL", fn);
+    return hip_status(focus::launch_compact(batch, B, keep, idx, cu_ret,
+                                            (hipStream_t)stream),
+                      "compaction launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status focus_retained_attn_workspace(int batch, int Hq, int Hkv, int d,
+                                           int max_prefix, int n_ret,
+                                           int max_ret, size_t* bytes) {
+  const char* fn = "focus_retained_attn_workspace";
+  if (bytes == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  focus_status st = check_attn_shape(fn, FOCUS_BF16, batch, 1, Hq, Hkv, d, max_prefix);
+  if (st != FOCUS_OK) return st;
+  if (n_ret < 0 || max_ret < 0)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: n_ret %d / max_ret %d < 0", fn, n_ret, max_ret);
+  *bytes = 0;
+  return ok();
+}
+
+focus_status focus_retained_attn(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q_src, const void* k_src, const void* v_src,
+    const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
+    const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
+    int max_prefix, void* out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* fn = "focus_retained_attn";
+  try {
+    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
+    if (st != FOCUS_OK) return st;
+    if (n_ret < 0) return fail(FOCUS_ERR_INVALID_ARG, "%s: n_ret %d < 0", fn, n_ret);
+    if (max_ret < 0 || max_ret > B)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret %d outside [0, B=%d]", fn,
+                  max_ret, B);
+    if (n_ret > 0 && max_ret == 0)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret is 0 but n_ret is %d", fn, n_ret);
+    if (n_ret == 0) return ok();
+    REQUIRE_PTR(q_src);
+    REQUIRE_PTR(k_src);
+    REQUIRE_PTR(v_src);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(cu_ret);
+    REQUIRE_PTR(cu_prefix);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(workspace);
+    if (max_prefix > 0) {
+      REQUIRE_PTR(k_cache);
+      REQUIRE_PTR(v_cache);
+    }
+    size_t need = 0;
+    st = focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
+                                       max_ret, &need);
+    if (st != FOCUS_OK) return st;
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
+                  fn, workspace_bytes, need);
+    focus::AttnArgs a = {};
+    a.q = q_src;
+    a.k_blk = k_src;
+    a.v_blk = v_src;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cu_prefix = cu_prefix;
+    a.idx = idx;
+    a.cu_ret = cu_ret;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.rph = max_ret;
+    head_chunks(a.G, max_ret, &a.hpw, &a.n_hc);
+    a.sl2 = log2_scale(scale, d);
+    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    return hip_status(
+        focus::launch_retained_attn(e, d, batch, a, (hipStream_t)stream),
+        "retained attention launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+}  // extern "C"

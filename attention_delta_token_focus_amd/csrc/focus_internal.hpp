@@ -1,0 +1,58 @@
+// Internal declarations shared by the libfocus translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace focus {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Key tile width of the attention kernels (keys per LDS tile).
+constexpr int kTile = 64;
+// Query rows per workgroup (4 waves x 32 rows, one 32x32 MFMA row block
+// per wave).
+constexpr int kRowsPerWG = 128;
+constexpr int kThreads = 256;
+
+struct AttnArgs {
+  const void* q;
+  const void* k_blk;
+  const void* v_blk;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_prefix;
+  const int32_t* idx;     // retained mode: gathered block rows
+  const int32_t* cu_ret;  // retained mode: per-sequence row offsets
+  void* out;
+  float* imp;             // block mode only
+  float* lse;             // block mode only, may be null
+  int B;                  // block size (rows per sequence in q/k_blk)
+  int Hq, Hkv, G;         // G = Hq / Hkv
+  int rph;                // query rows reserved per head in a workgroup
+  int hpw;                // query heads per workgroup
+  int n_hc;               // head chunks per KV head
+  float sl2;              // softmax scale * log2(e)
+};
+
+enum class Elem { F32 = 0, BF16 = 1 };
+
+// Launchers; return the launch status.
+hipError_t launch_block_attn(Elem e, int d, int batch, const AttnArgs& a,
+                             hipStream_t s);
+hipError_t launch_retained_attn(Elem e, int d, int batch, const AttnArgs& a,
+                                hipStream_t s);
+hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
+                             const float* imp0, const float* imp1,
+                             const int32_t* k_keep, uint8_t* keep, float* dI,
+                             hipStream_t s);
+hipError_t launch_compact(int batch, int B, const uint8_t* keep, int32_t* idx,
+                          int32_t* cu_ret, hipStream_t s);
+
+}  // namespace focus

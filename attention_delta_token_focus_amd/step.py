@@ -1,0 +1,118 @@
+"""One importance + evict block-step through the libfocus entry points.
+
+Order of calls per step (one stream, no host synchronisation):
+  focus_block_attn_importance on layer 0, then on layer 1;
+  focus_delta_topk (head mean, MaxPool1D, delta, top-K);
+  focus_compact (retained indices and per-sequence offsets);
+  focus_retained_attn once per further layer.
+This module only allocates the output buffers (torch device memory) and
+calls the binding; it computes nothing itself.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (dtype_code, focus_block_attn_importance,
+               focus_block_attn_importance_workspace, focus_compact,
+               focus_delta_topk, focus_retained_attn,
+               focus_retained_attn_workspace)
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    batch: int
+    block: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: torch.dtype
+    pool_k: int = 3
+    scale: float = 0.0  # <= 0: 1/sqrt(head_dim)
+
+
+def retained_counts(k_keep_host: Sequence[int], block: int):
+    """n_ret and max_ret known on the host from the budgets alone: top-K
+    keeps exactly min(max(K_b, 0), B) tokens of sequence b."""
+    kb = np.clip(np.asarray(k_keep_host, dtype=np.int64), 0, block)
+    return int(kb.sum()), int(kb.max()) if len(kb) else 0
+
+
+class FocusStep:
+    """Buffers and calls for one block-step over a fixed batch."""
+
+    def __init__(self, dims: Dims, cu_prefix_host: Sequence[int],
+                 k_keep_host: Sequence[int], n_further: int = 0,
+                 device="cuda", with_lse: bool = False):
+        self.dims = dims
+        dv = torch.device(device)
+        n, blk, hq, d = dims.batch, dims.block, dims.hq, dims.head_dim
+        cu = np.asarray(cu_prefix_host, dtype=np.int64)
+        self.max_prefix = int(np.diff(cu).max()) if n else 0
+        self.cu_prefix = torch.as_tensor(cu.astype(np.int32), device=dv)
+        self.k_keep = torch.as_tensor(
+            np.asarray(k_keep_host, dtype=np.int32), device=dv)
+        self.n_ret, self.max_ret = retained_counts(k_keep_host, blk)
+        f32 = dict(device=dv, dtype=torch.float32)
+        self.out = [torch.empty((n * blk, hq, d), device=dv, dtype=dims.dtype)
+                    for _ in range(2)]
+        self.imp = [torch.empty((n, hq, blk), **f32) for _ in range(2)]
+        self.lse = ([torch.empty((n, hq, blk), **f32) for _ in range(2)]
+                    if with_lse else [None, None])
+        self.dI = torch.empty((n, blk), **f32)
+        self.keep = torch.empty((n, blk), device=dv, dtype=torch.uint8)
+        self.idx = torch.empty((max(n * blk, 1),), device=dv,
+                               dtype=torch.int32)
+        self.cu_ret = torch.empty((n + 1,), device=dv, dtype=torch.int32)
+        self.ret_out = [torch.empty((max(self.n_ret, 1), hq, d), device=dv,
+                                    dtype=dims.dtype)
+                        for _ in range(n_further)]
+        ws_a = focus_block_attn_importance_workspace(
+            n, blk, hq, dims.hkv, d, self.max_prefix)
+        ws_r = focus_retained_attn_workspace(
+            n, hq, dims.hkv, d, self.max_prefix, self.n_ret, self.max_ret)
+        self.ws_bytes = max(ws_a, ws_r)
+        self.ws = (torch.empty((self.ws_bytes,), device=dv, dtype=torch.uint8)
+                   if self.ws_bytes else None)
+
+    # -- single calls -----------------------------------------------------
+    def block_attn(self, layer: Dict[str, torch.Tensor], which: int,
+                   stream=None) -> None:
+        dm = self.dims
+        focus_block_attn_importance(
+            dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
+            dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
+            layer["k_cache"], layer["v_cache"], self.cu_prefix,
+            self.max_prefix, self.out[which], self.imp[which],
+            self.lse[which], self.ws, self.ws_bytes, stream)
+
+    def select(self, stream=None) -> None:
+        dm = self.dims
+        focus_delta_topk(dm.batch, dm.block, dm.hq, dm.pool_k, self.imp[0],
+                         self.imp[1], self.k_keep, self.keep, self.dI, stream)
+        focus_compact(dm.batch, dm.block, self.keep, self.idx, self.cu_ret,
+                      stream)
+
+    def retained(self, layer: Dict[str, torch.Tensor], which: int,
+                 stream=None) -> None:
+        dm = self.dims
+        focus_retained_attn(
+            dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
+            dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
+            self.idx, self.cu_ret, self.n_ret, self.max_ret,
+            layer["k_cache"], layer["v_cache"], self.cu_prefix,
+            self.max_prefix, self.ret_out[which], self.ws, self.ws_bytes,
+            stream)
+
+    # -- the whole step ---------------------------------------------------
+    def run(self, layers: List[Dict[str, torch.Tensor]], stream=None) -> None:
+        """layers[0], layers[1]: importance layers; layers[2:]: further
+        layers run on the retained tokens."""
+        self.block_attn(layers[0], 0, stream)
+        self.block_attn(layers[1], 1, stream)
+        self.select(stream)
+        for i, lay in enumerate(layers[2:2 + len(self.ret_out)]):
+            self.retained(lay, i, stream)

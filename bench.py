@@ -1,0 +1,277 @@
+"""Benchmark of the FOCUS importance + evict block-step on one MI355X.
+
+One step = one pass of the whole hot path over one batch:
+  block attention + importance on layer 0 and on layer 1,
+  head mean / MaxPool1D / importance delta / top-K,
+  compaction of the retained tokens,
+  retained-query attention for each further layer (one at the default
+  workload, 34 at the full-step workload).
+Inputs are seeded synthetic tensors made on the device before timing.
+
+Prints one JSON line. `value` is block-steps/s (sequences through the step
+per second). `roofline` is for the dominant kernel (block attention +
+importance), timed with HIP events around each of its launches inside the
+timed region. `cpu_baseline` times the float64 oracle on a bounded sample of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = ("block-steps/sec at B=32, batch 256 (importance+evict); "
+          "% of HBM peak BW")
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "attention_delta_token_focus_amd", "csrc",
+                        "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_attn_c3.json")
+
+
+def attn_bytes(cfg, prefix_lens, with_lse=False) -> int:
+    """Algorithmic HBM bytes of one block-attention launch: Q in, O out,
+    prefix K/V and block K/V in, importance out (and lse if written)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    n, blk, hq, hkv, d = cfg.batch, cfg.block, cfg.hq, cfg.hkv, cfg.head_dim
+    per_seq = 2 * blk * hq * d * e + 2 * blk * hkv * d * e + 4 * hq * blk
+    if with_lse:
+        per_seq += 4 * hq * blk
+    return int(n * per_seq + 2 * int(prefix_lens.sum()) * hkv * d * e)
+
+
+def select_bytes(cfg, n_ret) -> int:
+    n, blk, hq = cfg.batch, cfg.block, cfg.hq
+    topk = n * (2 * 4 * hq * blk + blk + 4 * blk + 4)
+    compact = n * blk + 4 * n_ret + 4 * (n + 1)
+    return int(topk + compact)
+
+
+def retained_bytes(cfg, prefix_lens, n_ret) -> int:
+    e = 2 if cfg.dtype == "bf16" else 4
+    hq, hkv, d = cfg.hq, cfg.hkv, cfg.head_dim
+    return int(n_ret * (2 * hq * d * e + 2 * hkv * d * e + 4)
+               + 2 * int(prefix_lens.sum()) * hkv * d * e)
+
+
+def source_sha(path) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(cfg_name):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, only
+    if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != source_sha(ATTN_SRC) or \
+            t.get("workload") != cfg_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, n_further, budget_s=20.0):
+    """The oracle, as it stands, on a deterministic stride sample of the
+    workload's sequences (same tensors), growing the sample until about
+    budget_s seconds of CPU work."""
+    import oracle
+    from workloads import to_f32_numpy
+    cfg = inp.cfg
+    cu = inp.cu_prefix.astype(np.int64)
+    blk = cfg.block
+    order = list(range(0, cfg.batch, 16)) + [b for b in range(cfg.batch)
+                                            if b % 16]
+    done, t_used = 0, 0.0
+    chunk = 4
+    while done < cfg.batch and t_used < budget_s:
+        seqs = order[done:done + chunk]
+        layers = []
+        for lay in inp.layers[:2 + n_further]:
+            d = {}
+            for name in ("q", "k_blk", "v_blk"):
+                d[name] = np.concatenate([to_f32_numpy(
+                    lay[name][b * blk:(b + 1) * blk]) for b in seqs])
+            for name in ("k_cache", "v_cache"):
+                d[name] = np.concatenate([to_f32_numpy(
+                    lay[name][int(cu[b]):int(cu[b + 1])]) for b in seqs])
+            layers.append(d)
+        lens = np.array([cu[b + 1] - cu[b] for b in seqs])
+        sub_cu = np.concatenate([[0], np.cumsum(lens)])
+        t0 = time.perf_counter()
+        oracle.block_step(layers[0], layers[1], sub_cu, inp.meta.k_keep[seqs],
+                          blk, cfg.hq, cfg.hkv, cfg.pool_k,
+                          further_layers=layers[2:])
+        t_used += time.perf_counter() - t0
+        done += len(seqs)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return {
+        "value": done / t_used, "unit": "block-steps/s", "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"{done} of {cfg.batch} sequences (every 16th first, then "
+                   f"the rest in order) of the same workload and tensors, "
+                   f"float64 numpy, {t_used:.1f} s of CPU time"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (PMC scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the path shards "
+              "by sequence with no exchange, so run it once per GPU.",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    from attention_delta_token_focus_amd.step import Dims, FocusStep
+
+    cfg = workloads.get(args.config)
+    n_further = 1 if cfg.extra_layers == 0 else cfg.extra_layers
+    print(f"[bench] generating {cfg.name} on the device", file=sys.stderr,
+          flush=True)
+    inp = workloads.make_inputs(cfg, args.seed, device="cuda",
+                                n_layers=2 + n_further)
+    plen = inp.meta.prefix_lens
+    dims = Dims(cfg.batch, cfg.block, cfg.hq, cfg.hkv, cfg.head_dim,
+                workloads.torch_dtype(cfg), cfg.pool_k)
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=n_further)
+    layers = inp.layers
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step.run(layers)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr,
+          flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        step.block_attn(layers[0], 0)
+        e[1].record(stream)
+        step.block_attn(layers[1], 1)
+        e[2].record(stream)
+        step.select()
+        e[3].record(stream)
+        for i, lay in enumerate(layers[2:2 + n_further]):
+            step.retained(lay, i)
+        e[4].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+
+    attn_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)] + \
+              [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+    sel_ms = [ev[s][2].elapsed_time(ev[s][3]) for s in range(args.steps)]
+    ret_ms = [ev[s][3].elapsed_time(ev[s][4]) for s in range(args.steps)]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    a_bytes = attn_bytes(cfg, plen)
+    achieved = a_bytes / attn_avg_s / 1e9
+    ms_per_step = total_ms / args.steps
+    value = cfg.batch * args.steps / (total_ms / 1e3)
+    n_ret = step.n_ret
+    step_bytes = 2 * a_bytes + select_bytes(cfg, n_ret) + \
+        n_further * retained_bytes(cfg, plen, n_ret)
+    imp_evict_ms = float(np.mean(attn_ms)) * 2 + float(np.mean(sel_ms))
+
+    traffic = load_traffic(cfg.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, lognormal prefix lengths; "
+                "no model weights, no datasets)",
+        "config": {
+            "workload": cfg.name, "batch": cfg.batch, "block": cfg.block,
+            "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.head_dim,
+            "prefix_tokens": int(plen.sum()),
+            "prefix": (f"fixed {cfg.prefix_fixed}" if cfg.prefix_fixed else
+                       "lognormal median %g sigma %g clipped [%d, %d]"
+                       % cfg.prefix_lognormal),
+            "retained_tokens": n_ret, "pool_k": cfg.pool_k,
+            "further_layers": n_further, "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "block attention + importance (attn_kernel<false, bf16, 128>)",
+            "algorithmic_bytes_per_launch": a_bytes,
+            "avg_launch_us": round(attn_avg_s * 1e6, 2),
+        },
+        "breakdown_us": {
+            "block_attn_per_layer": round(float(np.mean(attn_ms)) * 1e3, 2),
+            "delta_topk_compact": round(float(np.mean(sel_ms)) * 1e3, 2),
+            "retained_attn_all_further_layers": round(float(np.mean(ret_ms)) * 1e3, 2),
+        },
+        "importance_evict_block_steps_per_s": round(
+            cfg.batch / (imp_evict_ms / 1e3), 1),
+        "step_hbm_fraction": round(step_bytes / (ms_per_step / 1e3) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+        "wall_s": round(wall, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, n_further, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

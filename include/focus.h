@@ -1,0 +1,186 @@
+/*
+ * libfocus: the token-eviction hot path of FOCUS for block-diffusion LLM
+ * decoding, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes: the pith.science review page of
+ * "FOCUS: DLLMs Know How to Tame Their Compute Bound" (arXiv 2601.23278),
+ * cited as "Pith page", and the sciencestack.ai summary page of the same
+ * paper, cited as "ScienceStack page".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array pointer is caller-owned DEVICE memory, contiguous,
+ *    row-major and 16-byte aligned. The library keeps no pointer after a
+ *    call returns, allocates no device memory and holds no global state.
+ *  - Outputs must not alias inputs.
+ *  - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    default stream) and never synchronises. Device-side faults surface at
+ *    the caller's next synchronisation.
+ *  - Device arrays (cu_prefix, k_keep, cu_ret, idx, keep) are never read on
+ *    the host. Host integers documented as promises (max_prefix, n_ret,
+ *    max_ret) must be true upper bounds / counts; the kernels clamp where
+ *    stated and otherwise trust them.
+ *  - Host-visible arguments are checked before any launch; a failed check
+ *    enqueues nothing and returns an error code. focus_last_error() then
+ *    gives a thread-local description. No C++ exception crosses this ABI.
+ *  - Element types: FOCUS_BF16 tensors hold bfloat16, FOCUS_F32 float32.
+ *    Accumulation is float32 in both cases; O is rounded to the tensor type
+ *    with round-to-nearest-even. Importances and lse are float32.
+ *  - Supported shapes: 1 <= B <= 128, head_dim d in {64, 128}, Hq a
+ *    multiple of Hkv. Query head h reads KV head h / (Hq / Hkv).
+ *  - Calls are reentrant and thread-safe.
+ */
+#ifndef FOCUS_H_
+#define FOCUS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FOCUS_OK = 0,
+  FOCUS_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misaligned pointer */
+  FOCUS_ERR_UNSUPPORTED = 2,  /* valid but not built: d, dtype, Hq % Hkv   */
+  FOCUS_ERR_WORKSPACE = 3,    /* workspace smaller than the queried size    */
+  FOCUS_ERR_HIP = 4           /* a HIP runtime call or launch failed        */
+} focus_status;
+
+typedef enum { FOCUS_F32 = 0, FOCUS_BF16 = 1 } focus_dtype;
+
+/* Library version string, e.g. "libfocus 0.1.0 gfx950". Static storage. */
+const char* focus_version(void);
+
+/* Name of a status code. Static storage. */
+const char* focus_status_string(focus_status s);
+
+/* Thread-local description of the last non-OK status returned on this
+ * thread ("" if none). Valid until the next libfocus call on the thread. */
+const char* focus_last_error(void);
+
+/* Workspace bytes that focus_block_attn_importance needs for these sizes.
+ * Writes *bytes; never fails for valid sizes. */
+focus_status focus_block_attn_importance_workspace(
+    int batch, int B, int Hq, int Hkv, int d, int max_prefix, size_t* bytes);
+
+/*
+ * Block attention with importance (one layer).
+ *
+ * Follows the Pith page, "What carries the argument": the importance I_j of
+ * block token j is the sum, over all B block queries, of the softmax
+ * attention weight that token j receives; the softmax runs along each query
+ * row (Referee Report, minor comment on Eq. 2). Every block query attends
+ * to its sequence's P_b prefix tokens and to all B block tokens, with no
+ * mask. Layers 0 and 1 are each one call ("The pith": the first two layers
+ * run on the whole block).
+ *
+ * Per sequence b (block rows b*B .. b*B+B-1, prefix tokens
+ * cu_prefix[b] .. cu_prefix[b+1]-1) and query head h with KV head
+ * g = h / (Hq/Hkv):
+ *    s_ij  = scale * q_i . k_j   over the P_b prefix keys then the B block keys
+ *    lse_i = log sum_j exp(s_ij)                       (natural log)
+ *    out_i = sum_j exp(s_ij - lse_i) v_j
+ *    imp[b,h,j] = sum_{i<B} exp(s_i,(P_b+j) - lse_i)   for block token j < B
+ *
+ *  dt          FOCUS_BF16 or FOCUS_F32 (type of q, k_*, v_*, out).
+ *  scale       softmax scale; <= 0 means 1/sqrt(d).
+ *  q           [batch*B, Hq, d]
+ *  k_blk,v_blk [batch*B, Hkv, d]   the block tokens' keys / values
+ *  k_cache,v_cache [cu_prefix[batch], Hkv, d]  packed prefix KV, sequence
+ *              after sequence
+ *  cu_prefix   device int32 [batch+1], cu_prefix[0] = 0, non-decreasing.
+ *  max_prefix  host promise: max_b P_b (sizes the launch).
+ *  out         [batch*B, Hq, d] attention output (type dt).
+ *  imp         float32 [batch, Hq, B] importance of the block columns.
+ *  lse         float32 [batch, Hq, B] natural-log row lse, or NULL.
+ *  workspace   device scratch of at least the queried size (may be NULL if
+ *              that size is 0); its contents on entry do not matter.
+ * Errors: INVALID_ARG (null required pointer, batch < 1, B not in [1,128],
+ * Hq or Hkv < 1, max_prefix < 0, misaligned pointer), UNSUPPORTED (d not
+ * 64/128, bad dt, Hq % Hkv != 0), WORKSPACE, HIP.
+ */
+focus_status focus_block_attn_importance(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk,
+    const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
+    int max_prefix, void* out, float* imp, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Head mean, MaxPool1D smoothing, importance delta and per-sequence top-K.
+ *
+ * Follows the Pith page, "What carries the argument": the importance is
+ * smoothed by MaxPool1D (kernel 3 in the Free-Parameter Ledger, Eq. 15),
+ * the delta is layer-1 minus layer-0 importance (Eq. 3), and the top
+ * candidates by delta are kept under the budget (also ScienceStack page,
+ * Fig. 5). Per sequence b and block position j:
+ *    Ibar_l[j]  = (1/Hq) sum_h imp_l[b,h,j]              (l = 0, 1)
+ *    Itil_l[j]  = max{ Ibar_l[t] : |t - j| <= (pool_k-1)/2, 0 <= t < B }
+ *    dI[b,j]    = Itil_1[j] - Itil_0[j]
+ *    keep[b,j]  = 1 for the min(max(k_keep[b],0),B) largest dI[b,.],
+ *                 equal values ordered by lower j first; else 0.
+ *
+ *  imp0, imp1  float32 [batch, Hq, B] from focus_block_attn_importance on
+ *              layer 0 and layer 1.
+ *  k_keep      device int32 [batch] budgets, clamped to [0, B].
+ *  keep        uint8 [batch, B] output, 0/1.
+ *  dI          float32 [batch, B] output, or NULL.
+ * Errors: INVALID_ARG (null required pointer, batch < 1, B not in [1,128],
+ * Hq < 1), UNSUPPORTED (pool_k even, < 1 or > 255), HIP.
+ */
+focus_status focus_delta_topk(
+    int batch, int B, int Hq, int pool_k, const float* imp0,
+    const float* imp1, const int32_t* k_keep, uint8_t* keep, float* dI,
+    void* stream);
+
+/*
+ * Stream compaction of the retained tokens: the tokens kept by top-K go on
+ * to the remaining layers (Pith page, "The pith").
+ *    idx    = every b*B + j with keep[b,j] != 0, b ascending, then j
+ *             ascending; int32, capacity batch*B (entries past the total are
+ *             left untouched).
+ *    cu_ret = int32 [batch+1]: cu_ret[0] = 0, cu_ret[b+1] - cu_ret[b] = the
+ *             number kept in sequence b.
+ * Errors: INVALID_ARG (null pointer, batch < 1, B not in [1,128]), HIP.
+ */
+focus_status focus_compact(int batch, int B, const uint8_t* keep,
+                           int32_t* idx, int32_t* cu_ret, void* stream);
+
+/* Workspace bytes that focus_retained_attn needs for these sizes. */
+focus_status focus_retained_attn_workspace(
+    int batch, int Hq, int Hkv, int d, int max_prefix, int n_ret,
+    int max_ret, size_t* bytes);
+
+/*
+ * Retained-query attention for one further layer: the layers after the
+ * first two run only on the retained tokens (Pith page, "The pith"). Every
+ * retained query of sequence b attends to that layer's P_b prefix keys and
+ * to the block keys of b's retained tokens only (no mask).
+ *
+ *  q_src       [batch*B, Hq, d]  the layer's block queries; rows read via idx.
+ *  k_src,v_src [batch*B, Hkv, d] the layer's block keys/values; via idx.
+ *  idx, cu_ret from focus_compact (device).
+ *  n_ret       host promise: cu_ret[batch] (rows of out).
+ *  max_ret     host promise: max_b (cu_ret[b+1] - cu_ret[b]), <= B.
+ *  k_cache,v_cache,cu_prefix,max_prefix  as in focus_block_attn_importance,
+ *              for this layer.
+ *  out         [n_ret, Hq, d] (type dt), row r is the query of idx[r].
+ * n_ret == 0 enqueues nothing and returns FOCUS_OK.
+ * Errors: as focus_block_attn_importance, plus INVALID_ARG for n_ret < 0 or
+ * max_ret outside [0, B] or max_ret == 0 < n_ret.
+ */
+focus_status focus_retained_attn(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q_src, const void* k_src, const void* v_src,
+    const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
+    const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
+    int max_prefix, void* out, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOCUS_H_ */

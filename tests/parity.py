@@ -1,0 +1,206 @@
+"""Helpers for comparing the HIP path with the float64 oracle.
+
+Both sides read the same seeded tensors: the HIP path on the device, the
+oracle after an exact widening to float32 (and float64 inside the oracle).
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from workloads import to_f32_numpy
+
+# Acceptance bars: the benchmark spec's tolerances, and tighter internal bars that
+# the fp32-accumulating kernels are expected to meet.
+TOL = {"bf16": dict(out=2e-2, imp=2e-2), "f32": dict(out=1e-5, imp=1e-5)}
+# The bf16 output bar scales with max|O|: probabilities enter the PV MFMA
+# as bf16 and O is stored as bf16, each a relative rounding of 2^-9.
+TIGHT = {"bf16": dict(out=4e-3, imp=1e-4, lse=1e-4, dI=1e-5),
+         "f32": dict(out=1e-5, imp=1e-5, lse=1e-5, dI=1e-6)}
+GAP = 1e-4  # K-th / (K+1)-th delta gap under which a selection is excused
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(inp: workloads.Inputs, device="cuda") -> List[Dict[str, torch.Tensor]]:
+    return [{k: v.to(device) for k, v in lay.items()} for lay in inp.layers]
+
+
+def dims_of(cfg: workloads.FocusConfig):
+    from attention_delta_token_focus_amd.step import Dims
+    return Dims(cfg.batch, cfg.block, cfg.hq, cfg.hkv, cfg.head_dim,
+                workloads.torch_dtype(cfg), cfg.pool_k)
+
+
+def run_gpu(inp: workloads.Inputs, layers_dev=None, n_further: Optional[int] = None,
+            with_lse: bool = True, step=None):
+    """Runs one block-step on the GPU; returns (step object, host results)."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    cfg = inp.cfg
+    if layers_dev is None:
+        layers_dev = to_device(inp)
+    if n_further is None:
+        n_further = len(layers_dev) - 2
+    if step is None:
+        step = FocusStep(dims_of(cfg), inp.cu_prefix, inp.meta.k_keep,
+                         n_further=n_further, with_lse=with_lse)
+    step.run(layers_dev)
+    torch.cuda.synchronize()
+    res = dict(
+        out=[to_f32_numpy(o) for o in step.out],
+        imp=[i.cpu().numpy() for i in step.imp],
+        lse=[l.cpu().numpy() if l is not None else None for l in step.lse],
+        dI=step.dI.cpu().numpy(), keep=step.keep.cpu().numpy(),
+        idx=step.idx.cpu().numpy()[:step.n_ret],
+        cu_ret=step.cu_ret.cpu().numpy(),
+        ret=[to_f32_numpy(r)[:step.n_ret] for r in step.ret_out])
+    return step, res
+
+
+def sub_layers(layers, cu_prefix, block: int, seqs: Sequence[int]):
+    """float32 numpy copies of the tensors of sequences `seqs`, repacked."""
+    cu = np.asarray(cu_prefix, dtype=np.int64)
+    out = []
+    for lay in layers:
+        d = {}
+        for name in ("q", "k_blk", "v_blk"):
+            d[name] = np.concatenate(
+                [to_f32_numpy(lay[name][b * block:(b + 1) * block]) for b in seqs])
+        for name in ("k_cache", "v_cache"):
+            d[name] = np.concatenate(
+                [to_f32_numpy(lay[name][int(cu[b]):int(cu[b + 1])]) for b in seqs])
+        out.append(d)
+    lens = np.array([cu[b + 1] - cu[b] for b in seqs])
+    sub_cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return out, sub_cu
+
+
+def rows_of(arr, seqs, block):
+    return np.concatenate([arr[b * block:(b + 1) * block] for b in seqs])
+
+
+@dataclasses.dataclass
+class SelectionReport:
+    exact: int = 0
+    excused: int = 0
+    failed: List[str] = dataclasses.field(default_factory=list)
+
+
+def check_selection(keep_gpu_b, dI_ref_b, k_b, label, rep: SelectionReport):
+    """Bit-exact retained set, unless the oracle's K-th/(K+1)-th gap is
+    below GAP; then every clearly-above token must be kept, none of the
+    clearly-below ones, and exactly K in total."""
+    blk = len(dI_ref_b)
+    kb = min(max(int(k_b), 0), blk)
+    order = sorted(range(blk), key=lambda j: (-dI_ref_b[j], j))
+    ref = set(order[:kb])
+    got = set(np.flatnonzero(keep_gpu_b).tolist())
+    if got == ref:
+        rep.exact += 1
+        return
+    ok = len(got) == kb and 0 < kb < blk
+    if ok:
+        top, nxt = dI_ref_b[order[kb - 1]], dI_ref_b[order[kb]]
+        ok = top - nxt < GAP
+        must = {j for j in range(blk) if dI_ref_b[j] >= top + GAP}
+        never = {j for j in range(blk) if dI_ref_b[j] <= nxt - GAP}
+        ok = ok and must <= got and not (never & got)
+    if ok:
+        rep.excused += 1
+    else:
+        rep.failed.append(f"{label}: gpu {sorted(got)} oracle {sorted(ref)}")
+
+
+def assert_close(name, got, ref, tol, tight=None, rel_scale=False):
+    if rel_scale and tight is not None and np.size(ref):
+        tight = tight * max(1.0, float(np.max(np.abs(ref))))
+    err = float(np.max(np.abs(np.asarray(got, np.float64) - ref))) if np.size(ref) else 0.0
+    log(f"  {name}: max abs err {err:.3e} (bar {tol:.1e}"
+        + (f", internal {tight:.1e})" if tight is not None else ")"))
+    assert err <= tol, f"{name}: max abs err {err} > {tol}"
+    if tight is not None:
+        assert err <= tight, f"{name}: max abs err {err} > internal bar {tight}"
+    return err
+
+
+def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=None,
+                 further_check: bool = True) -> SelectionReport:
+    """Oracle block-step on sequences `seqs` against the GPU results."""
+    cfg = inp.cfg
+    blk, kind = cfg.block, cfg.dtype
+    seqs = list(seqs)
+    layers = layers_host if layers_host is not None else inp.layers
+    sub, sub_cu = sub_layers(layers, inp.cu_prefix, blk, seqs)
+    k_keep = inp.meta.k_keep[seqs]
+    o = [oracle.block_attn_importance(sub[l]["q"], sub[l]["k_blk"], sub[l]["v_blk"],
+                                      sub[l]["k_cache"], sub[l]["v_cache"], sub_cu,
+                                      blk, cfg.hq, cfg.hkv) for l in (0, 1)]
+    for l in (0, 1):
+        assert_close(f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
+                     TOL[kind]["out"], TIGHT[kind]["out"], rel_scale=True)
+        assert_close(f"imp L{l}", res["imp"][l][seqs], o[l][1], TOL[kind]["imp"],
+                     TIGHT[kind]["imp"])
+        if res["lse"][l] is not None:
+            assert_close(f"lse L{l}", res["lse"][l][seqs], o[l][2], TIGHT[kind]["lse"])
+    dI_ref = oracle.importance_delta(o[0][1], o[1][1], cfg.pool_k)
+    assert_close("dI", res["dI"][seqs], dI_ref, TIGHT[kind]["dI"])
+
+    # The GPU's selection is a valid top-K of the GPU's own delta: every
+    # kept position beats every evicted one, equal deltas by lower index.
+    for b in seqs:
+        d_b, k_b = res["dI"][b], res["keep"][b]
+        kept, evicted = np.flatnonzero(k_b), np.flatnonzero(k_b == 0)
+        for j in kept:
+            bad = evicted[(d_b[evicted] > d_b[j]) |
+                          ((d_b[evicted] == d_b[j]) & (evicted < j))]
+            assert bad.size == 0, f"seq {b}: kept {j} loses to {bad.tolist()}"
+
+    # Retained sets against the oracle's own selection.
+    keep_ref = oracle.topk_keep(dI_ref, k_keep)
+    idx_ref, cu_ref = oracle.compact(keep_ref)
+    rep = SelectionReport()
+    exact = []
+    for i, b in enumerate(seqs):
+        before = rep.exact
+        check_selection(res["keep"][b], dI_ref[i], k_keep[i], f"seq {b}", rep)
+        if rep.exact > before:
+            exact.append(i)
+    log(f"  selection: {rep.exact} exact, {rep.excused} excused (gap < {GAP}), "
+        f"{len(rep.failed)} failed")
+    assert not rep.failed, rep.failed[:5]
+
+    # Compaction: offsets follow the budgets for the whole batch; the index
+    # list of every exactly matched sequence equals the oracle's.
+    kb_all = np.clip(inp.meta.k_keep, 0, blk)
+    assert res["cu_ret"][0] == 0 and np.array_equal(np.diff(res["cu_ret"]), kb_all)
+    g_cu = res["cu_ret"]
+    for i in exact:
+        b = seqs[i]
+        mine = res["idx"][g_cu[b]:g_cu[b + 1]] - b * blk
+        ref_j = idx_ref[cu_ref[i]:cu_ref[i + 1]] - i * blk
+        assert np.array_equal(mine, ref_j), f"seq {b}: idx {mine} vs {ref_j}"
+
+    # Retained attention, oracle on its own retained set; compared on the
+    # sequences whose set matched exactly.
+    if further_check and res["ret"]:
+        for li, ret in enumerate(res["ret"]):
+            lay = sub[2 + li]
+            ref = oracle.retained_attn(lay["q"], lay["k_blk"], lay["v_blk"], idx_ref,
+                                       cu_ref, lay["k_cache"], lay["v_cache"], sub_cu,
+                                       blk, cfg.hq, cfg.hkv)
+            if not exact:
+                continue
+            got = np.concatenate([ret[g_cu[seqs[i]]:g_cu[seqs[i] + 1]] for i in exact])
+            want = np.concatenate([ref[cu_ref[i]:cu_ref[i + 1]] for i in exact])
+            assert_close(f"retained L{2 + li}", got, want, TOL[kind]["out"],
+                         TIGHT[kind]["out"], rel_scale=True)
+    return rep

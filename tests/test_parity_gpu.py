@@ -1,0 +1,130 @@
+"""HIP path vs the float64 oracle, element by element (needs an MI355X).
+
+Small cases run the oracle on every sequence; the full-size workloads are
+checked on sampled sequences that the oracle computes one by one. Every
+call goes through the C ABI of libfocus (via the thin Python binding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import parity
+from tests.parity import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, cfg, seed=0, n_layers=None, prefix_lens=None, k_keep=None,
+          seqs=None):
+    log(f"[parity] {name}: N={cfg.batch} B={cfg.block} Hq={cfg.hq} "
+        f"Hkv={cfg.hkv} d={cfg.head_dim} {cfg.dtype} seed={seed}")
+    inp = workloads.make_inputs(cfg, seed, n_layers=n_layers,
+                                prefix_lens=prefix_lens, k_keep=k_keep)
+    step, res = parity.run_gpu(inp)
+    rep = parity.compare_step(inp, res, range(cfg.batch) if seqs is None else seqs)
+    return inp, step, res, rep
+
+
+def test_c1_tiny_f32():
+    _case("c1", workloads.get("c1"), n_layers=3)
+
+
+def test_c2_bf16_full():
+    _case("c2", workloads.get("c2"), n_layers=3)
+
+
+def test_c3_reduced_batch():
+    cfg = workloads.scaled(workloads.get("c3"), batch=24)
+    _case("c3 reduced", cfg, n_layers=3)
+
+
+def test_c4_reduced_batch():
+    cfg = workloads.scaled(workloads.get("c4"), batch=3)
+    _case("c4 reduced", cfg, n_layers=3)
+
+
+def test_c5_reduced_batch_several_layers():
+    cfg = workloads.scaled(workloads.get("c5"), batch=6, extra_layers=3)
+    _case("c5 reduced", cfg)
+
+
+EDGE = [
+    # name, overrides, prefix lengths, budgets
+    ("B1 P0/1/63 d64", dict(block=1, hq=4, hkv=1, head_dim=64), [0, 1, 63], [0, 1, 1]),
+    ("B7 G8 ragged", dict(block=7, hq=8, hkv=1), [0, 65, 129], [0, 3, 7]),
+    ("B64 G4 tile edges", dict(block=64, hq=8, hkv=2), [63, 64, 1], [1, 32, 64]),
+    ("B128 P4096 full budget", dict(block=128, hq=8, hkv=2, pool_k=5), [4096], [128]),
+    ("B128 ragged", dict(block=128, hq=4, hkv=1), [0, 127, 129], [0, 1, 31]),
+    ("f32 d64 G1", dict(dtype="f32", head_dim=64, hq=4, hkv=4), [5, 77], [3, 32]),
+    ("f32 d128 G2", dict(dtype="f32", head_dim=128, hq=4, hkv=2), [64, 0], [8, 8]),
+    ("bf16 d64 G8 B32", dict(head_dim=64, hq=16, hkv=2), [100, 300], [11, 6]),
+    ("B16 G8 two chunks", dict(block=16, hq=16, hkv=1), [33, 17], [4, 16]),
+    ("B33 G4", dict(block=33, hq=8, hkv=2), [31, 200], [10, 33]),
+]
+
+
+@pytest.mark.parametrize("name,over,plens,kk", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, over, plens, kk):
+    base = workloads.get("c2")
+    cfg = workloads.scaled(base, batch=len(plens), prefix_fixed=1, **over)
+    _case(name, cfg, n_layers=3, prefix_lens=plens, k_keep=kk)
+
+
+def test_retained_with_full_budget_equals_block_attention():
+    """Cross-call pin: keeping every token, retained attention on layer L
+    must reproduce block attention's output for layer L."""
+    cfg = workloads.scaled(workloads.get("c3"), batch=5)
+    log("[parity] cross pin retained == block attention")
+    inp = workloads.make_inputs(cfg, 3, n_layers=2, k_keep=[32] * 5)
+    lay = parity.to_device(inp)
+    lay = [lay[0], lay[1], lay[1]]       # further layer = layer 1 itself
+    step, res = parity.run_gpu(inp, layers_dev=lay)
+    assert step.n_ret == 5 * 32
+    assert np.array_equal(res["idx"], np.arange(160))
+    got, ref = res["ret"][0], res["out"][1]
+    err = float(np.abs(got - ref).max())
+    log(f"  retained vs block max abs diff {err:.3e}")
+    assert err <= 1e-6
+
+
+def test_deterministic_bitwise():
+    cfg = workloads.scaled(workloads.get("c3"), batch=8)
+    log("[parity] determinism")
+    inp = workloads.make_inputs(cfg, 5, n_layers=3)
+    lay = parity.to_device(inp)
+    step, r1 = parity.run_gpu(inp, layers_dev=lay)
+    _, r2 = parity.run_gpu(inp, layers_dev=lay)
+    for k in ("dI", "keep", "idx", "cu_ret"):
+        assert np.array_equal(r1[k], r2[k]), k
+    for k in ("out", "imp", "lse", "ret"):
+        for a, b in zip(r1[k], r2[k]):
+            assert np.array_equal(a, b), k
+
+
+def _full_size(name, cfg_name, seqs_pick, n_layers=None):
+    cfg = workloads.get(cfg_name)
+    log(f"[parity] full size {name}: generating on the device")
+    inp = workloads.make_inputs(cfg, 0, device="cuda", n_layers=n_layers)
+    plen = inp.meta.prefix_lens
+    seqs = sorted(set(seqs_pick(plen)))
+    log(f"  sequences checked: {seqs} (P_b {[int(plen[s]) for s in seqs]})")
+    step, res = parity.run_gpu(inp, layers_dev=inp.layers)
+    parity.compare_step(inp, res, seqs, layers_host=inp.layers)
+    # properties that hold at any size
+    kb = np.clip(inp.meta.k_keep, 0, cfg.block)
+    assert np.array_equal(res["keep"].sum(axis=1), kb)
+    assert np.array_equal(np.diff(res["cu_ret"]), kb)
+    imp_sum = res["imp"][0].sum(axis=2)
+    assert (imp_sum > 0).all() and (imp_sum <= cfg.block * (1 + 1e-5)).all()
+    del inp, step
+    torch.cuda.empty_cache()
+
+
+def test_c3_full_size_sampled():
+    _full_size("c3", "c3", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 0,
+                                      17, 128, 255], n_layers=3)
+
+
+def test_c5_full_size_sampled():
+    _full_size("c5", "c5", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 64])
