@@ -114,7 +114,7 @@ focus_status focus_block_attn_importance_workspace(int batch, int B, int Hq,
   if (bytes == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
   focus_status st = check_attn_shape(fn, FOCUS_BF16, batch, B, Hq, Hkv, d, max_prefix);
   if (st != FOCUS_OK) return st;
-  *bytes = 0;
+  *bytes = focus::order_workspace_bytes(batch);
   return ok();
 }
 
@@ -163,6 +163,10 @@ focus_status focus_block_attn_importance(
     a.rph = B;
     head_chunks(a.G, B, &a.hpw, &a.n_hc);
     a.sl2 = log2_scale(scale, d);
+    a.order = static_cast<int32_t*>(workspace);
+    hipError_t he = focus::launch_lpt_order(batch, cu_prefix, static_cast<int32_t*>(workspace),
+                                            (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
     const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
     return hip_status(focus::launch_block_attn(e, d, batch, a, (hipStream_t)stream),
                       "block attention launch");
@@ -222,7 +226,7 @@ focus_status focus_retained_attn_workspace(int batch, int Hq, int Hkv, int d,
   if (st != FOCUS_OK) return st;
   if (n_ret < 0 || max_ret < 0)
     return fail(FOCUS_ERR_INVALID_ARG, "%s: n_ret %d / max_ret %d < 0", fn, n_ret, max_ret);
-  *bytes = 0;
+  *bytes = focus::order_workspace_bytes(batch);
   return ok();
 }
 
@@ -280,6 +284,10 @@ focus_status focus_retained_attn(
     a.rph = max_ret;
     head_chunks(a.G, max_ret, &a.hpw, &a.n_hc);
     a.sl2 = log2_scale(scale, d);
+    a.order = static_cast<int32_t*>(workspace);
+    hipError_t he = focus::launch_lpt_order(batch, cu_prefix, static_cast<int32_t*>(workspace),
+                                            (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
     const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
     return hip_status(
         focus::launch_retained_attn(e, d, batch, a, (hipStream_t)stream),

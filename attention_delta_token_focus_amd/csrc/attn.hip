@@ -128,7 +128,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
   const int hc = wid % a.n_hc;
   wid /= a.n_hc;
   const int g = wid % a.Hkv;
-  const int b = wid / a.Hkv;
+  const int rank = wid / a.Hkv;
+  const int b = a.order != nullptr ? a.order[rank] : rank;
 
   const int p0 = a.cu_prefix[b];
   const int plen = a.cu_prefix[b + 1] - p0;
@@ -441,11 +442,13 @@ hipError_t launch(Elem e, int d, int batch, const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_block_attn(Elem e, int d, int batch, const AttnArgs& a,
                              hipStream_t s) {
+  if (e == Elem::BF16 && d == 128) return launch_block_attn_bf16(batch, a, s);
   return launch<false>(e, d, batch, a, s);
 }
 
 hipError_t launch_retained_attn(Elem e, int d, int batch, const AttnArgs& a,
                                 hipStream_t s) {
+  if (e == Elem::BF16 && d == 128) return launch_retained_attn_bf16(batch, a, s);
   return launch<true>(e, d, batch, a, s);
 }
 

@@ -1,0 +1,461 @@
+// Block attention with importance, and retained-query attention: the bf16,
+// head_dim 128 kernel tuned for gfx950 (MI355X).
+//
+// Same computation as the generic kernel in attn.hip (see there for the
+// sources on the pages); this file only changes how the work is mapped on
+// the chip:
+//  * K/V tiles of 32 keys travel HBM -> LDS by direct-to-LDS loads
+//    (global_load_lds_dwordx4) through a ring of 4 stages, so three tiles
+//    are in flight while one is computed and no registers hold loads.
+//    Completion is tracked by hand: each wave waits until its own loads for
+//    the tile are done (vmcnt), then one barrier per tile publishes them.
+//  * K rows sit in LDS with their 16-byte chunks XOR-swizzled by the row
+//    (conflict-free ds_read_b128 operand reads). V stays key-major in LDS
+//    and the O^T = V^T P^T operand is read with ds_read_b64_tr_b16, which
+//    hands each lane 4 consecutive keys of one head-dim column.
+//  * Online softmax with the scale folded into one FMA per score and a
+//    lazy rescale of O: the running max only moves (and O is only rescaled)
+//    when a row max grows by more than 2^8; the final O / l and lse are
+//    exact whatever max was used.
+//  * The block keys are processed first and their raw scores stay in
+//    registers, so the importance pass needs neither a reload nor a
+//    recompute once the final lse is known.
+//  * Work items are visited longest prefix first (order from a one-block
+//    bitonic sort of the prefix lengths), the 8 KV heads of a sequence on
+//    neighbouring workgroups.
+#include "focus_internal.hpp"
+
+namespace focus {
+namespace {
+
+constexpr int TK = 32;          // keys per tile
+constexpr int NSTAGE = 4;       // ring depth
+constexpr int D = 128;
+constexpr int ROWB = D * 2;     // bytes per key row (256)
+constexpr int TILEB = TK * ROWB;        // 8 KB per K or V tile
+constexpr int STAGEB = 2 * TILEB;       // K + V
+constexpr int PPITCH = TK + 4;          // fp32 probability row pitch
+constexpr int SMEM = NSTAGE * STAGEB;   // 64 KB
+static_assert(kRowsPerWG * PPITCH * 4 <= SMEM, "pass-2 buffer fits the ring");
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;   // log2 headroom before O is rescaled
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// Wait until at most `n` of this wave's vector-memory operations are
+// outstanding (n in {0, 4, 8}), then barrier. The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wait_and_barrier(int n) {
+  if (n >= 8) {
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else if (n >= 4) {
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+
+// The eight V^T operand fragments of one 16-key step: for head-dim tiles
+// dt = 0..3 (addresses a0..a3) the keys at row offset +0 and +8 rows
+// (+2048 bytes), each read with ds_read_b64_tr_b16. The reads sit in one
+// asm block that also waits for them, so no output register is ever left
+// with a load in flight (and the compiler adds no wait of its own for the
+// direct-to-LDS loads that may still be landing in other ring stages).
+#define FOCUS_TR8(OFF0, OFF1)                                                 \
+  asm volatile(                                                               \
+      "ds_read_b64_tr_b16 %0, %8 offset:" #OFF0 "\n\t"                        \
+      "ds_read_b64_tr_b16 %1, %8 offset:" #OFF1 "\n\t"                        \
+      "ds_read_b64_tr_b16 %2, %9 offset:" #OFF0 "\n\t"                        \
+      "ds_read_b64_tr_b16 %3, %9 offset:" #OFF1 "\n\t"                        \
+      "ds_read_b64_tr_b16 %4, %10 offset:" #OFF0 "\n\t"                       \
+      "ds_read_b64_tr_b16 %5, %10 offset:" #OFF1 "\n\t"                       \
+      "ds_read_b64_tr_b16 %6, %11 offset:" #OFF0 "\n\t"                       \
+      "ds_read_b64_tr_b16 %7, %11 offset:" #OFF1 "\n\t"                       \
+      "s_waitcnt lgkmcnt(0)"                                                  \
+      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]), "=v"(f[4]),           \
+        "=v"(f[5]), "=v"(f[6]), "=v"(f[7])                                    \
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)                                    \
+      : "memory")
+
+template <int ST>
+__device__ __forceinline__ void v_frags(uint32_t a0, uint32_t a1, uint32_t a2,
+                                        uint32_t a3, u32x2v (&f)[8]) {
+  if constexpr (ST == 0) {
+    FOCUS_TR8(0, 2048);
+  } else {
+    FOCUS_TR8(4096, 6144);
+  }
+}
+
+__device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <bool RET, int NBT>
+__global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int half = lane >> 5;
+
+  int wid = blockIdx.x;
+  const int hc = wid % a.n_hc;
+  wid /= a.n_hc;
+  const int g = wid % a.Hkv;
+  const int rank = wid / a.Hkv;
+  const int b = a.order != nullptr ? a.order[rank] : rank;
+
+  const int p0 = a.cu_prefix[b];
+  const int plen = a.cu_prefix[b + 1] - p0;
+  int rbase, nq;
+  if constexpr (RET) {
+    rbase = a.cu_ret[b];
+    nq = a.cu_ret[b + 1] - rbase;
+    if (nq <= 0) return;  // uniform over the workgroup
+  } else {
+    rbase = b * a.B;
+    nq = a.B;
+  }
+  const int nh = min(a.hpw, a.G - hc * a.hpw);
+  const int r = wave * 32 + n;
+  const int hl = r / a.rph;
+  const int qi = r - hl * a.rph;
+  const bool row_ok = (hl < nh) && (qi < nq);
+  const int h = g * a.G + hc * a.hpw + hl;
+  const bool wave_on = wave * 32 < nh * a.rph;
+
+  // ---- loader geometry: lane covers row (4j + lane/16) of DMA slot j,
+  // physical 16-byte chunk lane%16.
+  const int lrow0 = 8 * wave + (lane >> 4);   // rows lrow0 and lrow0 + 4
+  const int pchunk = lane & 15;
+  const int nbt = (nq + TK - 1) / TK;        // block tiles (<= NBT)
+  const int npt = (plen + TK - 1) / TK;
+  const int nt = nbt + npt;
+
+  // Block rows this lane loads (gathered in retained mode), resolved up
+  // front so that no index load sits between the streaming loads.
+  int brow[NBT][2];
+#pragma unroll
+  for (int bt = 0; bt < NBT; ++bt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int j = bt * TK + lrow0 + 4 * i;
+      j = min(j, nq - 1);  // rows past the end repeat the last row (masked)
+      if constexpr (RET) {
+        brow[bt][i] = bt < nbt ? a.idx[rbase + j] : 0;
+      } else {
+        brow[bt][i] = rbase + j;
+      }
+    }
+  }
+
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const char* kb = static_cast<const char*>(a.k_blk);
+  const char* vb = static_cast<const char*>(a.v_blk);
+  const size_t rowstride = (size_t)a.Hkv * ROWB;  // bytes between tokens
+  const size_t goff = (size_t)g * ROWB;
+
+  auto issue_tile = [&](int t) {
+    char* st = smem + (t % NSTAGE) * STAGEB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int lr = lrow0 + 4 * i;          // row inside the tile
+      size_t row;
+      const char *ksrc, *vsrc;
+      if (t < nbt) {
+        int rr = 0;
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt)
+          if (bt == t) rr = brow[bt][i];
+        row = (size_t)rr;
+        ksrc = kb;
+        vsrc = vb;
+      } else {
+        const int pt = t - nbt;
+        row = (size_t)(p0 + min(pt * TK + lr, plen - 1));
+        ksrc = kc;
+        vsrc = vc;
+      }
+      const size_t base = row * rowstride + goff;
+      const int kch = pchunk ^ (lr & 15);
+      const int vch = pchunk ^ ((lr & 3) << 1);
+      char* dst = st + (2 * wave + i) * 1024;
+      dma16(ksrc + base + kch * 16, dst);
+      dma16(vsrc + base + vch * 16, dst + TILEB);
+    }
+  };
+
+  // Q^T operand: lane (row n, half) holds d = 16s + 8*half .. +7.
+  bf16x8 qf[8];
+  {
+    const __bf16* qp = nullptr;
+    if (row_ok) {
+      const int qrow = RET ? a.idx[rbase + qi] : rbase + qi;
+      qp = static_cast<const __bf16*>(a.q) + ((size_t)qrow * a.Hq + h) * D;
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * half)
+                     : bf16x8{};
+  }
+
+  // Prologue: tiles 0 .. NSTAGE-2 in flight. All index and Q loads are
+  // consumed first so that vmcnt below counts ring loads only.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int t = 0; t < NSTAGE - 1 && t < nt; ++t) issue_tile(t);
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+  f32x16 sblk[NBT];
+#pragma unroll
+  for (int bt = 0; bt < NBT; ++bt) sblk[bt] = f32x16{};
+  float mrun = -INFINITY;  // max used for the exponentials (log2 domain)
+  float lsum = 0.f;        // this lane's share of the row sum
+  const float c = a.sl2;
+
+  // Per-lane LDS read offsets.
+  const int krd = n * ROWB;                       // + ((2s+half)^(n&15))*16
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int ve = l16 >> 2, vq = l16 & 3;
+  const int vh = grp >> 1;
+  // V^T operand read: row (16*st + 8*x + 4*vh + ve), logical chunk
+  // 4*dt + 2*(grp&1) + vq/2, swizzled by 2*ve, byte 8*(vq&1).
+  const int vrow_base = 4 * vh + ve;
+  const int vchunk_base = 2 * (grp & 1) + (vq >> 1);
+  const int vbyte = 8 * (vq & 1);
+
+  for (int t = 0; t < nt; ++t) {
+    // Loads issued after tile t so far: min(nt, t + NSTAGE - 1) - (t + 1).
+    const int ahead = min(nt, t + NSTAGE - 1) - (t + 1);
+    wait_and_barrier(4 * ahead);
+    if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
+    if (!wave_on) continue;
+
+    const char* ks = smem + (t % NSTAGE) * STAGEB;
+    const char* vs = ks + TILEB;
+    const int cnt = t < nbt ? min(TK, nq - t * TK) : min(TK, plen - (t - nbt) * TK);
+
+    f32x16 s = {};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int ch = (2 * k + half) ^ (n & 15);
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(ks + krd + ch * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], s, 0, 0, 0);
+    }
+    if (cnt < TK) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 8 * (v >> 2) + 4 * half + (v & 3);
+        if (key >= cnt) s[v] = -INFINITY;
+      }
+    }
+    if constexpr (!RET) {
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt)
+        if (bt == t) sblk[bt] = s;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    if (__any(mx > mrun + kLazy)) {
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
+      s[v] = p;
+      ps += p;
+    }
+    lsum += ps;
+
+    {
+      // V^T fragment addresses for this stage, one per head-dim tile.
+      uint32_t va[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        va[dt] = lds_addr(vs) + vrow_base * ROWB +
+                 (((4 * dt + vchunk_base) ^ (2 * ve)) << 4) + vbyte;
+      u32x2v f0[8], f1[8];
+      v_frags<0>(va[0], va[1], va[2], va[3], f0);
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[e]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            cat8(f0[2 * dt], f0[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
+      v_frags<1>(va[0], va[1], va[2], va[3], f1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 + e]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            cat8(f1[2 * dt], f1[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
+    }
+  }
+
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float lse2 = mrun + log2f(ltot);
+
+  if (wave_on && row_ok) {
+    const float inv = 1.0f / ltot;
+    __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)(rbase + qi) * a.Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * half) = o;
+      }
+    }
+    if constexpr (!RET) {
+      if (a.lse != nullptr && half == 0)
+        a.lse[((size_t)b * a.Hq + h) * a.B + qi] = lse2 * kLn2;
+    }
+  }
+
+  if constexpr (!RET) {
+    // Importance of the block columns: exp2(s*c - lse2) from the kept raw
+    // block scores, summed down each column per head in a fixed order.
+    float* pbuf = reinterpret_cast<float*>(smem);
+    for (int bt = 0; bt < nbt; ++bt) {
+      const int cnt = min(TK, nq - bt * TK);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (wave_on) {
+        f32x16 sb = {};
+#pragma unroll
+        for (int k = 0; k < NBT; ++k)
+          if (k == bt) sb = sblk[k];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[4 * q4 + e], c, -lse2));
+          *reinterpret_cast<f32x4*>(pbuf + r * PPITCH + 8 * q4 + 4 * half) = pv;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int id = tid; id < nh * TK; id += kThreads) {
+        const int hh = id / TK;
+        const int key = id - hh * TK;
+        if (key < cnt) {
+          float acc = 0.f;
+          const float* col = pbuf + (hh * a.rph) * PPITCH + key;
+          for (int i = 0; i < a.B; ++i) acc += col[i * PPITCH];
+          const int hg = g * a.G + hc * a.hpw + hh;
+          a.imp[((size_t)b * a.Hq + hg) * a.B + bt * TK + key] = acc;
+        }
+      }
+    }
+  }
+}
+
+// Longest-prefix-first visiting order of the sequences: bitonic sort of
+// (P_b, ~b) in LDS by one workgroup, descending; equal lengths keep the
+// lower sequence first. Batches above kMaxSort keep their natural order.
+constexpr int kMaxSort = 8192;
+
+__global__ void __launch_bounds__(1024) lpt_order_kernel(
+    int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kMaxSort];
+  const int tid = threadIdx.x;
+  if (batch > kMaxSort) {
+    for (int i = tid; i < batch; i += 1024) order[i] = i;
+    return;
+  }
+  int n2 = 1;
+  while (n2 < batch) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) {
+    uint64_t k = 0;
+    if (i < batch) {
+      const uint32_t len = (uint32_t)(cu_prefix[i + 1] - cu_prefix[i]);
+      k = ((uint64_t)len << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += 1024) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t x = key[i], y = key[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? x < y : x > y) {
+            key[i] = y;
+            key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < batch; i += 1024)
+    order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
+}
+
+template <bool RET>
+hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)batch * a.Hkv * a.n_hc), block(kThreads);
+  switch (nbt) {
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<RET, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<RET, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<RET, 4>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+int block_tiles(int rows) {
+  const int t = (rows + TK - 1) / TK;
+  return t <= 1 ? 1 : (t <= 2 ? 2 : 4);
+}
+
+}  // namespace
+
+size_t order_workspace_bytes(int batch) {
+  return ((size_t)batch * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
+  return launch_nbt<false>(block_tiles(a.B), batch, a, s);
+}
+
+hipError_t launch_retained_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
+  return launch_nbt<true>(block_tiles(a.rph), batch, a, s);
+}
+
+}  // namespace focus

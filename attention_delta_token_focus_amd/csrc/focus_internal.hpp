@@ -30,6 +30,7 @@ struct AttnArgs {
   const int32_t* cu_prefix;
   const int32_t* idx;     // retained mode: gathered block rows
   const int32_t* cu_ret;  // retained mode: per-sequence row offsets
+  const int32_t* order;   // visiting order of the sequences (may be null)
   void* out;
   float* imp;             // block mode only
   float* lse;             // block mode only, may be null
@@ -48,6 +49,14 @@ hipError_t launch_block_attn(Elem e, int d, int batch, const AttnArgs& a,
                              hipStream_t s);
 hipError_t launch_retained_attn(Elem e, int d, int batch, const AttnArgs& a,
                                 hipStream_t s);
+// Tuned bf16 / head_dim 128 kernels (attn_bf16.hip).
+hipError_t launch_block_attn_bf16(int batch, const AttnArgs& a, hipStream_t s);
+hipError_t launch_retained_attn_bf16(int batch, const AttnArgs& a, hipStream_t s);
+// Longest-prefix-first order of the sequences into `order` [batch].
+hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
+                            hipStream_t s);
+size_t order_workspace_bytes(int batch);
+
 hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
                              const int32_t* k_keep, uint8_t* keep, float* dI,

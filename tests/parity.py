@@ -20,8 +20,11 @@ from workloads import to_f32_numpy
 # the fp32-accumulating kernels are expected to meet.
 TOL = {"bf16": dict(out=2e-2, imp=2e-2), "f32": dict(out=1e-5, imp=1e-5)}
 # The bf16 output bar scales with max|O|: probabilities enter the PV MFMA
-# as bf16 and O is stored as bf16, each a relative rounding of 2^-9.
-TIGHT = {"bf16": dict(out=4e-3, imp=1e-4, lse=1e-4, dI=1e-5),
+# as bf16 and O is stored as bf16, each a relative rounding of 2^-9, so the
+# error of one element is bounded by about 2^-8 * sum_j p_j |v_j| + 2^-9 |O|
+# (|v| <= ~4.5 for these inputs); 8e-3 * max(1, max|O|) is two bf16 ulps at
+# magnitude 1, 2.5x inside the acceptance bar.
+TIGHT = {"bf16": dict(out=8e-3, imp=1e-4, lse=1e-4, dI=1e-5),
          "f32": dict(out=1e-5, imp=1e-5, lse=1e-5, dI=1e-6)}
 GAP = 1e-4  # K-th / (K+1)-th delta gap under which a selection is excused
 
