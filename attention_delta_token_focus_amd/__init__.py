@@ -39,7 +39,7 @@ lib_path = os.path.join(_PKG, "lib", "libfocus.so")
 if not os.path.exists(lib_path):
     raise ImportError(
         f"libfocus is not built ({lib_path} missing); build it with "
-        "`python -m attention_delta_token_focus_amd.build`")
+        "`python attention_delta_token_focus_amd/build.py`")
 
 _c = ctypes
 _P = _c.c_void_p

@@ -1,6 +1,8 @@
 """Build libfocus.so (all HIP sources under csrc/) for gfx950, in-tree.
 
-Usage: python -m attention_delta_token_focus_amd.build
+Usage: python attention_delta_token_focus_amd/build.py
+(run as a script: the package itself refuses to import until the library
+exists)
 """
 from __future__ import annotations
 

@@ -12,7 +12,10 @@
 //  * K rows sit in LDS with their 16-byte chunks XOR-swizzled by the row
 //    (conflict-free ds_read_b128 operand reads). V stays key-major in LDS
 //    and the O^T = V^T P^T operand is read with ds_read_b64_tr_b16, which
-//    hands each lane 4 consecutive keys of one head-dim column.
+//    hands each lane 4 consecutive keys of one head-dim column. The LDS
+//    serves 32 lanes of 8-byte reads per cycle; one such read touches 4 key
+//    rows x 64 bytes, so V's 16-byte chunks are XOR-swizzled by
+//    4 * (row mod 4), which spreads those 16 chunks over all banks.
 //  * Online softmax with the scale folded into one FMA per score and a
 //    lazy rescale of O: the running max only moves (and O is only rescaled)
 //    when a row max grows by more than 2^8; the final O / l and lse are
@@ -96,6 +99,20 @@ __device__ __forceinline__ void v_frags(uint32_t a0, uint32_t a1, uint32_t a2,
   } else {
     FOCUS_TR8(4096, 6144);
   }
+}
+
+// Max / sum of a value over the lane pair (l, l ^ 32), without LDS:
+// v_permlane32_swap exchanges the two 32-lane halves, so the pair of
+// results holds both values in every lane.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
@@ -194,7 +211,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
       }
       const size_t base = row * rowstride + goff;
       const int kch = pchunk ^ (lr & 15);
-      const int vch = pchunk ^ ((lr & 3) << 1);
+      const int vch = pchunk ^ ((lr & 3) << 2);
       char* dst = st + (2 * wave + i) * 1024;
       dma16(ksrc + base + kch * 16, dst);
       dma16(vsrc + base + vch * 16, dst + TILEB);
@@ -237,29 +254,47 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   const int ve = l16 >> 2, vq = l16 & 3;
   const int vh = grp >> 1;
   // V^T operand read: row (16*st + 8*x + 4*vh + ve), logical chunk
-  // 4*dt + 2*(grp&1) + vq/2, swizzled by 2*ve, byte 8*(vq&1).
+  // 4*dt + 2*(grp&1) + vq/2, swizzled by 4*ve, byte 8*(vq&1).
   const int vrow_base = 4 * vh + ve;
   const int vchunk_base = 2 * (grp & 1) + (vq >> 1);
   const int vbyte = 8 * (vq & 1);
 
-  for (int t = 0; t < nt; ++t) {
-    // Loads issued after tile t so far: min(nt, t + NSTAGE - 1) - (t + 1).
-    const int ahead = min(nt, t + NSTAGE - 1) - (t + 1);
-    wait_and_barrier(4 * ahead);
-    if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
-    if (!wave_on) continue;
-
+  // S^T of one tile (raw scores, unmasked): lane (row n, half) gets keys
+  // 8*(v/4) + 4*half + v%4, v = 0..15.
+  auto qk = [&](int t) -> f32x16 {
     const char* ks = smem + (t % NSTAGE) * STAGEB;
-    const char* vs = ks + TILEB;
-    const int cnt = t < nbt ? min(TK, nq - t * TK) : min(TK, plen - (t - nbt) * TK);
-
-    f32x16 s = {};
+    f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int ch = (2 * k + half) ^ (n & 15);
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(ks + krd + ch * 16);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], s, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[k], acc, 0, 0, 0);
     }
+    return acc;
+  };
+  auto tile_cnt = [&](int t) {
+    return t < nbt ? min(TK, nq - t * TK) : min(TK, plen - (t - nbt) * TK);
+  };
+
+  // Tile 0 must be in LDS before its scores; tiles 1.. may still land.
+  wait_and_barrier(4 * (min(nt, NSTAGE - 1) - 1));
+  f32x16 s_cur = {};
+  if (wave_on) s_cur = qk(0);
+
+  // Software pipeline: iteration t computes the scores of tile t + 1 on
+  // the matrix cores while the vector units run the softmax of tile t and
+  // its P V product. Tiles t and t + 1 are resident at the top of the
+  // iteration; the ring slot of tile t - 1 is then refilled with tile t + 3.
+  for (int t = 0; t < nt; ++t) {
+    wait_and_barrier(t + 2 < nt ? 4 : 0);
+    if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
+    if (!wave_on) continue;
+
+    f32x16 s_next = {};
+    if (t + 1 < nt) s_next = qk(t + 1);
+
+    f32x16 s = s_cur;
+    const int cnt = tile_cnt(t);
     if (cnt < TK) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -272,10 +307,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
       for (int bt = 0; bt < NBT; ++bt)
         if (bt == t) sblk[bt] = s;
     }
-    float mx = s[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    const float m4a = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const float m4b = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+    const float m4c = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
+    const float m4d = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
+    const float mx = pair_max(fmaxf(fmaxf(m4a, m4b), fmaxf(m4c, m4d))) * c;
     if (__any(mx > mrun + kLazy)) {
       const float mnew = fmaxf(mrun, mx);
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
@@ -284,22 +320,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
     }
-    float ps = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
-      s[v] = p;
-      ps += p;
-    }
-    lsum += ps;
+    for (int v = 0; v < 16; ++v)
+      s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
+    float q8[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) q8[v] = s[2 * v] + s[2 * v + 1];
+    lsum += ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
 
     {
+      const char* vs = smem + (t % NSTAGE) * STAGEB + TILEB;
       // V^T fragment addresses for this stage, one per head-dim tile.
       uint32_t va[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         va[dt] = lds_addr(vs) + vrow_base * ROWB +
-                 (((4 * dt + vchunk_base) ^ (2 * ve)) << 4) + vbyte;
+                 (((4 * dt + vchunk_base) ^ (4 * ve)) << 4) + vbyte;
       u32x2v f0[8], f1[8];
       v_frags<0>(va[0], va[1], va[2], va[3], f0);
       bf16x8 pb;
@@ -317,9 +353,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             cat8(f1[2 * dt], f1[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
     }
+    s_cur = s_next;
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = pair_sum(lsum);
   const float lse2 = mrun + log2f(ltot);
 
   if (wave_on && row_ok) {
@@ -378,17 +415,41 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   }
 }
 
-// Longest-prefix-first visiting order of the sequences: bitonic sort of
-// (P_b, ~b) in LDS by one workgroup, descending; equal lengths keep the
-// lower sequence first. Batches above kMaxSort keep their natural order.
+// Longest-prefix-first visiting order of the sequences; equal lengths keep
+// the lower sequence first. Up to 1024 sequences: thread i counts the
+// sequences that go before it (lengths broadcast from LDS, four per read)
+// and writes i at that rank. Up to kMaxSort: bitonic sort of (P_b, ~b) in
+// LDS. Larger batches keep their natural order.
 constexpr int kMaxSort = 8192;
 
 __global__ void __launch_bounds__(1024) lpt_order_kernel(
     int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
-  __shared__ uint64_t key[kMaxSort];
+  __shared__ __attribute__((aligned(16))) uint64_t key[kMaxSort];
   const int tid = threadIdx.x;
   if (batch > kMaxSort) {
     for (int i = tid; i < batch; i += 1024) order[i] = i;
+    return;
+  }
+  if (batch <= 1024) {
+    int* len = reinterpret_cast<int*>(key);
+    const int n4 = (batch + 3) & ~3;
+    int mine = 0;
+    if (tid < n4) {
+      mine = tid < batch ? cu_prefix[tid + 1] - cu_prefix[tid] : -1;
+      len[tid] = mine;
+    }
+    __syncthreads();
+    if (tid < batch) {
+      int rank = 0;
+      for (int j = 0; j < n4; j += 4) {
+        const int4 l4 = *reinterpret_cast<const int4*>(len + j);
+        rank += (l4.x > mine) + (l4.x == mine && j < tid);
+        rank += (l4.y > mine) + (l4.y == mine && j + 1 < tid);
+        rank += (l4.z > mine) + (l4.z == mine && j + 2 < tid);
+        rank += (l4.w > mine) + (l4.w == mine && j + 3 < tid);
+      }
+      order[rank] = tid;
+    }
     return;
   }
   int n2 = 1;

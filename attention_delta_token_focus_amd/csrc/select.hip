@@ -20,7 +20,65 @@ __device__ __forceinline__ uint32_t order_code(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Sum over heads of one block position for both layers, heads in
+// ascending order; eight heads' loads are issued before any is added.
+__device__ __forceinline__ void head_sums(const float* __restrict__ i0,
+                                          const float* __restrict__ i1, int Hq,
+                                          int B, int j, float& a0, float& a1) {
+  a0 = 0.f;
+  a1 = 0.f;
+  int h = 0;
+  for (; h + 8 <= Hq; h += 8) {
+    float x0[8], x1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      x0[u] = i0[(h + u) * B + j];
+      x1[u] = i1[(h + u) * B + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a0 += x0[u];
+      a1 += x1[u];
+    }
+  }
+  for (; h < Hq; ++h) {
+    a0 += i0[h * B + j];
+    a1 += i1[h * B + j];
+  }
+}
+
+// Bitonic sort of NS*64 slots (slot i = lane + 64*s) into descending
+// order, with lane shuffles; slot pairs of one lane compare in registers.
+template <int NS>
+__device__ __forceinline__ void bitonic_desc(uint64_t (&key)[2], int lane) {
+  constexpr int N = NS * 64;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int st = k >> 1; st > 0; st >>= 1) {
+      if (st == 64) {
+        // only when k == 128: descending merge of the two slots
+        const uint64_t hi = key[0] > key[1] ? key[0] : key[1];
+        const uint64_t lo = key[0] > key[1] ? key[1] : key[0];
+        key[0] = hi;
+        key[1] = lo;
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int i = lane + 64 * s;
+          const uint64_t other = __shfl_xor(key[s], st);
+          const bool take_max = ((i & st) == 0) == ((i & k) == 0);
+          const uint64_t mx = key[s] > other ? key[s] : other;
+          const uint64_t mn = key[s] > other ? other : key[s];
+          key[s] = take_max ? mx : mn;
+        }
+      }
+    }
+  }
+}
+
 // One wavefront per sequence. Lane l holds block positions l and l + 64.
+template <int NS>
 __global__ void __launch_bounds__(64) delta_topk_kernel(
     int B, int Hq, int radius, const float* __restrict__ imp0,
     const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
@@ -31,15 +89,13 @@ __global__ void __launch_bounds__(64) delta_topk_kernel(
   const float inv_h = 1.0f / (float)Hq;
   const float* i0 = imp0 + (size_t)b * Hq * B;
   const float* i1 = imp1 + (size_t)b * Hq * B;
+  const int kb = min(max(k_keep[b], 0), B);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int j = lane + 64 * s;
     if (j < B) {
-      float a0 = 0.f, a1 = 0.f;
-      for (int h = 0; h < Hq; ++h) {  // fixed head order
-        a0 += i0[h * B + j];
-        a1 += i1[h * B + j];
-      }
+      float a0, a1;
+      head_sums(i0, i1, Hq, B, j, a0, a1);
       mean[0][j] = a0 * inv_h;
       mean[1][j] = a1 * inv_h;
     }
@@ -49,11 +105,10 @@ __global__ void __launch_bounds__(64) delta_topk_kernel(
   // Sort keys: (order code of dI) << 32 | (~j), so that larger dI comes
   // first and, for equal dI, the lower position. Empty slots are 0, which
   // is below every real key.
-  uint64_t key[2];
+  uint64_t key[2] = {0, 0};
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int j = lane + 64 * s;
-    key[s] = 0;
     if (j < B) {
       const int lo = max(0, j - radius), hi = min(B - 1, j + radius);
       float m0 = -INFINITY, m1 = -INFINITY;
@@ -66,36 +121,9 @@ __global__ void __launch_bounds__(64) delta_topk_kernel(
       key[s] = ((uint64_t)order_code(d) << 32) | (uint32_t)(0xFFFFFFFFu - j);
     }
   }
-
-  // Bitonic sort of the 128 slots (index i = lane + 64*slot) into
-  // descending order.
-  for (int k = 2; k <= 128; k <<= 1) {
-    for (int st = k >> 1; st > 0; st >>= 1) {
-      if (st == 64) {
-        // partner is the other slot of the same lane; k == 128: descending
-        const uint64_t hi = key[0] > key[1] ? key[0] : key[1];
-        const uint64_t lo = key[0] > key[1] ? key[1] : key[0];
-        key[0] = hi;
-        key[1] = lo;
-      } else {
+  bitonic_desc<NS>(key, lane);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int i = lane + 64 * s;
-          const uint64_t other = __shfl_xor(key[s], st);
-          const bool lower = (i & st) == 0;
-          const bool desc = (i & k) == 0;
-          const bool take_max = (lower == desc);
-          const uint64_t mx = key[s] > other ? key[s] : other;
-          const uint64_t mn = key[s] > other ? other : key[s];
-          key[s] = take_max ? mx : mn;
-        }
-      }
-    }
-  }
-
-  const int kb = min(max(k_keep[b], 0), B);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int p = lane + 64 * s;  // rank in descending order
     if (key[s] != 0) {
       const int j = (int)(0xFFFFFFFFu - (uint32_t)key[s]);
@@ -105,23 +133,45 @@ __global__ void __launch_bounds__(64) delta_topk_kernel(
 }
 
 // One workgroup of 1024 threads walks the batch in chunks of 1024
-// sequences: per-sequence counts, a workgroup exclusive scan (wavefront
-// shuffles + LDS), then per sequence a ballot over the keep bytes whose
-// mbcnt rank places each kept index.
+// sequences. Thread t owns sequence base + t: it counts its kept bytes
+// (16-byte loads when rows are 16-byte aligned), the workgroup takes an
+// exclusive scan of the counts (wavefront shuffles + LDS), and the thread
+// writes its sequence's kept indices in ascending order.
+template <bool VEC>
 __global__ void __launch_bounds__(1024) compact_kernel(
     int batch, int B, const uint8_t* __restrict__ keep,
     int32_t* __restrict__ idx, int32_t* __restrict__ cu_ret) {
   __shared__ int wsum[16];
-  __shared__ int offs[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int carry = 0;
   for (int base = 0; base < batch; base += 1024) {
     const int b = base + tid;
+    const bool live = b < batch;
+    u32x4 row[8];  // up to 128 keep bytes
     int cnt = 0;
-    if (b < batch) {
+    if constexpr (VEC) {
+      const int nv = B >> 4;
+      const u32x4* kp = reinterpret_cast<const u32x4*>(keep + (size_t)b * B);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        row[v] = (live && v < nv) ? kp[v] : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x = row[v][w];
+          // bytes are 0/1 flags; count the non-zero ones
+          const uint32_t nz = ((x | (x >> 1) | (x >> 2) | (x >> 3) | (x >> 4) |
+                                (x >> 5) | (x >> 6) | (x >> 7)) & 0x01010101u);
+          cnt += __popc(nz);
+        }
+      }
+    } else if (live) {
       const uint8_t* kp = keep + (size_t)b * B;
+#pragma unroll 8
       for (int j = 0; j < B; ++j) cnt += kp[j] != 0;
     }
     int x = cnt;  // inclusive scan within the wavefront
@@ -142,23 +192,26 @@ __global__ void __launch_bounds__(1024) compact_kernel(
       if (lane < 16) wsum[lane] = w;
     }
     __syncthreads();
-    const int excl = carry + (wave ? wsum[wave - 1] : 0) + x - cnt;
-    if (b < batch) cu_ret[b] = excl;
-    offs[tid] = excl;
+    int off = carry + (wave ? wsum[wave - 1] : 0) + x - cnt;
     const int chunk_total = wsum[15];
-    __syncthreads();
-    for (int sb = wave * 64; sb < wave * 64 + 64; ++sb) {
-      const int bb = base + sb;
-      if (bb >= batch) break;
-      int off = offs[sb];
-      for (int j0 = 0; j0 < B; j0 += 64) {
-        const int j = j0 + lane;
-        const bool kept = j < B && keep[(size_t)bb * B + j] != 0;
-        const uint64_t m = __ballot(kept);
-        const int rank = __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (kept) idx[off + rank] = bb * B + j;
-        off += __popcll(m);
+    if (live) {
+      cu_ret[b] = off;
+      if constexpr (VEC) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = 16 * v + 4 * w + e;
+              if (j < B && ((row[v][w] >> (8 * e)) & 0xFFu) != 0) idx[off++] = b * B + j;
+            }
+          }
+        }
+      } else {
+        const uint8_t* kp = keep + (size_t)b * B;
+        for (int j = 0; j < B; ++j)
+          if (kp[j] != 0) idx[off++] = b * B + j;
       }
     }
     carry += chunk_total;
@@ -173,15 +226,26 @@ hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
                              const int32_t* k_keep, uint8_t* keep, float* dI,
                              hipStream_t s) {
-  hipLaunchKernelGGL(delta_topk_kernel, dim3(batch), dim3(64), 0, s, B, Hq,
-                     (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+  if (B <= 64) {
+    hipLaunchKernelGGL(delta_topk_kernel<1>, dim3(batch), dim3(64), 0, s, B, Hq,
+                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+  } else {
+    hipLaunchKernelGGL(delta_topk_kernel<2>, dim3(batch), dim3(64), 0, s, B, Hq,
+                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_compact(int batch, int B, const uint8_t* keep, int32_t* idx,
                           int32_t* cu_ret, hipStream_t s) {
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, batch, B, keep,
-                     idx, cu_ret);
+  // 16-byte row loads need 16-byte aligned rows (B a multiple of 16).
+  if (B % 16 == 0 && (reinterpret_cast<uintptr_t>(keep) & 15u) == 0) {
+    hipLaunchKernelGGL(compact_kernel<true>, dim3(1), dim3(1024), 0, s, batch, B,
+                       keep, idx, cu_ret);
+  } else {
+    hipLaunchKernelGGL(compact_kernel<false>, dim3(1), dim3(1024), 0, s, batch, B,
+                       keep, idx, cu_ret);
+  }
   return hipGetLastError();
 }
 
