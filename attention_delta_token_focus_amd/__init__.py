@@ -21,7 +21,8 @@ __all__ = [
     "FocusError", "lib", "lib_path", "dtype_code", "focus_version",
     "focus_status_string", "focus_last_error",
     "focus_block_attn_importance_workspace", "focus_block_attn_importance",
-    "focus_delta_topk", "focus_compact", "focus_retained_attn_workspace",
+    "focus_delta_topk", "focus_compact", "focus_select", "focus_schedule",
+    "focus_retained_attn_workspace",
     "focus_retained_attn",
 ]
 
@@ -53,16 +54,18 @@ _SIGS = {
     "focus_last_error": (_c.c_char_p, []),
     "focus_block_attn_importance_workspace": (
         _I, [_I, _I, _I, _I, _I, _I, _c.POINTER(_SZ)]),
+    "focus_schedule": (_I, [_I, _P, _P, _P]),
     "focus_block_attn_importance": (
-        _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _I,
-             _P, _P, _P, _P, _SZ, _P]),
+        _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _P,
+             _I, _P, _P, _P, _P, _SZ, _P]),
     "focus_delta_topk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "focus_compact": (_I, [_I, _I, _P, _P, _P, _P]),
+    "focus_select": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "focus_retained_attn_workspace": (
         _I, [_I, _I, _I, _I, _I, _I, _I, _c.POINTER(_SZ)]),
     "focus_retained_attn": (
         _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _I, _I,
-             _P, _P, _P, _I, _P, _P, _SZ, _P]),
+             _P, _P, _P, _P, _I, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -133,8 +136,13 @@ def focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d,
     return n.value
 
 
+def focus_schedule(batch, cu_prefix, order, stream=None) -> None:
+    _check(lib.focus_schedule(batch, _ptr(cu_prefix, "cu_prefix"),
+                              _ptr(order, "order"), _stream(stream)))
+
+
 def focus_block_attn_importance(dt, batch, B, Hq, Hkv, d, scale, q, k_blk,
-                                v_blk, k_cache, v_cache, cu_prefix,
+                                v_blk, k_cache, v_cache, cu_prefix, order,
                                 max_prefix, out, imp, lse=None,
                                 workspace=None, workspace_bytes=0,
                                 stream=None) -> None:
@@ -142,7 +150,8 @@ def focus_block_attn_importance(dt, batch, B, Hq, Hkv, d, scale, q, k_blk,
         dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
         _ptr(q, "q"), _ptr(k_blk, "k_blk"), _ptr(v_blk, "v_blk"),
         _ptr(k_cache, "k_cache", True), _ptr(v_cache, "v_cache", True),
-        _ptr(cu_prefix, "cu_prefix"), max_prefix, _ptr(out, "out"),
+        _ptr(cu_prefix, "cu_prefix"), _ptr(order, "order", True),
+        max_prefix, _ptr(out, "out"),
         _ptr(imp, "imp"), _ptr(lse, "lse", True),
         _ptr(workspace, "workspace", True), workspace_bytes,
         _stream(stream)))
@@ -161,6 +170,14 @@ def focus_compact(batch, B, keep, idx, cu_ret, stream=None) -> None:
                              _ptr(cu_ret, "cu_ret"), _stream(stream)))
 
 
+def focus_select(batch, B, Hq, pool_k, imp0, imp1, k_keep, keep, dI, idx,
+                 cu_ret, stream=None) -> None:
+    _check(lib.focus_select(
+        batch, B, Hq, pool_k, _ptr(imp0, "imp0"), _ptr(imp1, "imp1"),
+        _ptr(k_keep, "k_keep"), _ptr(keep, "keep"), _ptr(dI, "dI", True),
+        _ptr(idx, "idx"), _ptr(cu_ret, "cu_ret"), _stream(stream)))
+
+
 def focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
                                   max_ret) -> int:
     n = _SZ(0)
@@ -171,7 +188,7 @@ def focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
 
 def focus_retained_attn(dt, batch, B, Hq, Hkv, d, scale, q_src, k_src,
                         v_src, idx, cu_ret, n_ret, max_ret, k_cache, v_cache,
-                        cu_prefix, max_prefix, out, workspace=None,
+                        cu_prefix, order, max_prefix, out, workspace=None,
                         workspace_bytes=0, stream=None) -> None:
     _check(lib.focus_retained_attn(
         dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
@@ -179,6 +196,6 @@ def focus_retained_attn(dt, batch, B, Hq, Hkv, d, scale, q_src, k_src,
         _ptr(idx, "idx", n_ret == 0), _ptr(cu_ret, "cu_ret", n_ret == 0),
         n_ret, max_ret, _ptr(k_cache, "k_cache", True),
         _ptr(v_cache, "v_cache", True), _ptr(cu_prefix, "cu_prefix"),
-        max_prefix, _ptr(out, "out", n_ret == 0),
+        _ptr(order, "order", True), max_prefix, _ptr(out, "out", n_ret == 0),
         _ptr(workspace, "workspace", True), workspace_bytes,
         _stream(stream)))

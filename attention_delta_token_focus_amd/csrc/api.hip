@@ -82,6 +82,22 @@ void head_chunks(int G, int rph, int* hpw, int* n_hc) {
   *n_hc = (G + per - 1) / per;
 }
 
+// Visiting order of the attention call: the caller's (from focus_schedule),
+// else the longest-prefix-first one written into the workspace by a
+// one-block kernel first. (Deriving it inside every attention workgroup was
+// measured slower: it delays the start of each workgroup's K/V stream.)
+hipError_t plan_order(int batch, const int32_t* cu_prefix, const int32_t* order,
+                      void* workspace, focus::AttnArgs* a, hipStream_t s) {
+  a->batch = batch;
+  if (order != nullptr) {
+    a->order = order;
+    return hipSuccess;
+  }
+  int32_t* own = static_cast<int32_t*>(workspace);
+  a->order = own;
+  return focus::launch_lpt_order(batch, cu_prefix, own, s);
+}
+
 float log2_scale(float scale, int d) {
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   return s * 1.4426950408889634f;
@@ -106,6 +122,20 @@ const char* focus_status_string(focus_status s) {
 
 const char* focus_last_error(void) { return tl_error.c_str(); }
 
+focus_status focus_schedule(int batch, const int32_t* cu_prefix, int32_t* order,
+                            void* stream) {
+  const char* fn = "focus_schedule";
+  try {
+    if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+    if (cu_prefix == nullptr || order == nullptr)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: cu_prefix and order must be non-NULL", fn);
+    return hip_status(focus::launch_lpt_order(batch, cu_prefix, order, (hipStream_t)stream),
+                      "schedule launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
 focus_status focus_block_attn_importance_workspace(int batch, int B, int Hq,
                                                    int Hkv, int d,
                                                    int max_prefix,
@@ -121,9 +151,9 @@ focus_status focus_block_attn_importance_workspace(int batch, int B, int Hq,
 focus_status focus_block_attn_importance(
     focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
     const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
-    const void* v_cache, const int32_t* cu_prefix, int max_prefix, void* out,
-    float* imp, float* lse, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    const void* v_cache, const int32_t* cu_prefix, const int32_t* order,
+    int max_prefix, void* out, float* imp, float* lse, void* workspace,
+    size_t workspace_bytes, void* stream) {
   const char* fn = "focus_block_attn_importance";
   try {
     focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
@@ -135,6 +165,7 @@ focus_status focus_block_attn_importance(
     REQUIRE_PTR(out);
     REQUIRE_PTR(imp);
     OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(order);
     OPTIONAL_PTR(workspace);
     if (max_prefix > 0) {
       REQUIRE_PTR(k_cache);
@@ -143,6 +174,7 @@ focus_status focus_block_attn_importance(
     size_t need = 0;
     st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);
     if (st != FOCUS_OK) return st;
+    if (order != nullptr) need = 0;  // the workspace only holds our own order
     if (workspace_bytes < need || (need > 0 && workspace == nullptr))
       return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
                   fn, workspace_bytes, need);
@@ -163,11 +195,9 @@ focus_status focus_block_attn_importance(
     a.rph = B;
     head_chunks(a.G, B, &a.hpw, &a.n_hc);
     a.sl2 = log2_scale(scale, d);
-    a.order = static_cast<int32_t*>(workspace);
-    hipError_t he = focus::launch_lpt_order(batch, cu_prefix, static_cast<int32_t*>(workspace),
-                                            (hipStream_t)stream);
-    if (he != hipSuccess) return hip_status(he, "work-order launch");
     const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
     return hip_status(focus::launch_block_attn(e, d, batch, a, (hipStream_t)stream),
                       "block attention launch");
   } catch (...) {
@@ -195,6 +225,31 @@ focus_status focus_delta_topk(int batch, int B, int Hq, int pool_k,
     return hip_status(focus::launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1,
                                                k_keep, keep, dI, (hipStream_t)stream),
                       "delta/top-K launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status focus_select(int batch, int B, int Hq, int pool_k, const float* imp0,
+                          const float* imp1, const int32_t* k_keep, uint8_t* keep,
+                          float* dI, int32_t* idx, int32_t* cu_ret, void* stream) {
+  const char* fn = "focus_select";
+  try {
+    if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+    if (B < 1 || B > 128)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
+    if (Hq < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d < 1", fn, Hq);
+    if (pool_k < 1 || pool_k > 255 || pool_k % 2 == 0)
+      return fail(FOCUS_ERR_UNSUPPORTED, "%s: pool_k %d must be odd in [1, 255]",
+                  fn, pool_k);
+    REQUIRE_PTR(imp0);
+    REQUIRE_PTR(imp1);
+    if (k_keep == nullptr || keep == nullptr || idx == nullptr || cu_ret == nullptr)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: k_keep, keep, idx and cu_ret must be non-NULL",
+                  fn);
+    return hip_status(focus::launch_select(batch, B, Hq, pool_k, imp0, imp1, k_keep, keep,
+                                           dI, idx, cu_ret, (hipStream_t)stream),
+                      "select launch");
   } catch (...) {
     return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
   }
@@ -235,8 +290,8 @@ focus_status focus_retained_attn(
     const void* q_src, const void* k_src, const void* v_src,
     const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
-    int max_prefix, void* out, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    const int32_t* order, int max_prefix, void* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
   const char* fn = "focus_retained_attn";
   try {
     focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
@@ -255,6 +310,7 @@ focus_status focus_retained_attn(
     REQUIRE_PTR(cu_ret);
     REQUIRE_PTR(cu_prefix);
     REQUIRE_PTR(out);
+    OPTIONAL_PTR(order);
     OPTIONAL_PTR(workspace);
     if (max_prefix > 0) {
       REQUIRE_PTR(k_cache);
@@ -264,6 +320,7 @@ focus_status focus_retained_attn(
     st = focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
                                        max_ret, &need);
     if (st != FOCUS_OK) return st;
+    if (order != nullptr) need = 0;  // the workspace only holds our own order
     if (workspace_bytes < need || (need > 0 && workspace == nullptr))
       return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
                   fn, workspace_bytes, need);
@@ -284,11 +341,9 @@ focus_status focus_retained_attn(
     a.rph = max_ret;
     head_chunks(a.G, max_ret, &a.hpw, &a.n_hc);
     a.sl2 = log2_scale(scale, d);
-    a.order = static_cast<int32_t*>(workspace);
-    hipError_t he = focus::launch_lpt_order(batch, cu_prefix, static_cast<int32_t*>(workspace),
-                                            (hipStream_t)stream);
-    if (he != hipSuccess) return hip_status(he, "work-order launch");
     const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
     return hip_status(
         focus::launch_retained_attn(e, d, batch, a, (hipStream_t)stream),
         "retained attention launch");

@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
   wid /= a.n_hc;
   const int g = wid % a.Hkv;
   const int rank = wid / a.Hkv;
-  const int b = a.order != nullptr ? a.order[rank] : rank;
+  const int b = a.order != nullptr ? min(max(a.order[rank], 0), a.batch - 1) : rank;
 
   const int p0 = a.cu_prefix[b];
   const int plen = a.cu_prefix[b + 1] - p0;

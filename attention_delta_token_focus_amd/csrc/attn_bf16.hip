@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   wid /= a.n_hc;
   const int g = wid % a.Hkv;
   const int rank = wid / a.Hkv;
-  const int b = a.order != nullptr ? a.order[rank] : rank;
+  const int b = a.order != nullptr ? min(max(a.order[rank], 0), a.batch - 1) : rank;
 
   const int p0 = a.cu_prefix[b];
   const int plen = a.cu_prefix[b + 1] - p0;
@@ -416,40 +416,42 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
 }
 
 // Longest-prefix-first visiting order of the sequences; equal lengths keep
-// the lower sequence first. Up to 1024 sequences: thread i counts the
-// sequences that go before it (lengths broadcast from LDS, four per read)
-// and writes i at that rank. Up to kMaxSort: bitonic sort of (P_b, ~b) in
-// LDS. Larger batches keep their natural order.
+// the lower sequence first. Up to 256 sequences: one 256-thread block,
+// thread i counts the sequences that go before sequence i (lengths
+// broadcast from LDS, four per read) and writes i at that rank. Up to
+// kMaxSort: bitonic sort of (P_b, ~b) in LDS by 1024 threads. Larger
+// batches keep their natural order.
 constexpr int kMaxSort = 8192;
+constexpr int kRankMax = 256;
 
-__global__ void __launch_bounds__(1024) lpt_order_kernel(
+__global__ void __launch_bounds__(256) lpt_rank_kernel(
     int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
-  __shared__ __attribute__((aligned(16))) uint64_t key[kMaxSort];
+  __shared__ __attribute__((aligned(16))) int len[kRankMax];
+  const int tid = threadIdx.x;
+  const int n4 = (batch + 3) & ~3;
+  int mine = -1;
+  if (tid < batch) mine = cu_prefix[tid + 1] - cu_prefix[tid];
+  if (tid < n4) len[tid] = mine;
+  __syncthreads();
+  if (tid < batch) {
+    int rank = 0;
+    for (int j = 0; j < n4; j += 4) {
+      const int4 l4 = *reinterpret_cast<const int4*>(len + j);
+      rank += (l4.x > mine) + (l4.x == mine && j < tid);
+      rank += (l4.y > mine) + (l4.y == mine && j + 1 < tid);
+      rank += (l4.z > mine) + (l4.z == mine && j + 2 < tid);
+      rank += (l4.w > mine) + (l4.w == mine && j + 3 < tid);
+    }
+    order[rank] = tid;
+  }
+}
+
+__global__ void __launch_bounds__(1024) lpt_sort_kernel(
+    int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kMaxSort];
   const int tid = threadIdx.x;
   if (batch > kMaxSort) {
     for (int i = tid; i < batch; i += 1024) order[i] = i;
-    return;
-  }
-  if (batch <= 1024) {
-    int* len = reinterpret_cast<int*>(key);
-    const int n4 = (batch + 3) & ~3;
-    int mine = 0;
-    if (tid < n4) {
-      mine = tid < batch ? cu_prefix[tid + 1] - cu_prefix[tid] : -1;
-      len[tid] = mine;
-    }
-    __syncthreads();
-    if (tid < batch) {
-      int rank = 0;
-      for (int j = 0; j < n4; j += 4) {
-        const int4 l4 = *reinterpret_cast<const int4*>(len + j);
-        rank += (l4.x > mine) + (l4.x == mine && j < tid);
-        rank += (l4.y > mine) + (l4.y == mine && j + 1 < tid);
-        rank += (l4.z > mine) + (l4.z == mine && j + 2 < tid);
-        rank += (l4.w > mine) + (l4.w == mine && j + 3 < tid);
-      }
-      order[rank] = tid;
-    }
     return;
   }
   int n2 = 1;
@@ -507,7 +509,11 @@ size_t order_workspace_bytes(int batch) {
 
 hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
                             hipStream_t s) {
-  hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
+  if (batch <= kRankMax) {
+    hipLaunchKernelGGL(lpt_rank_kernel, dim3(1), dim3(256), 0, s, batch, cu_prefix, order);
+  } else {
+    hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
+  }
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct AttnArgs {
   const int32_t* idx;     // retained mode: gathered block rows
   const int32_t* cu_ret;  // retained mode: per-sequence row offsets
   const int32_t* order;   // visiting order of the sequences (may be null)
+  int batch;              // number of sequences
   void* out;
   float* imp;             // block mode only
   float* lse;             // block mode only, may be null
@@ -61,6 +62,10 @@ hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
                              const int32_t* k_keep, uint8_t* keep, float* dI,
                              hipStream_t s);
+hipError_t launch_select(int batch, int B, int Hq, int pool_k,
+                         const float* imp0, const float* imp1,
+                         const int32_t* k_keep, uint8_t* keep, float* dI,
+                         int32_t* idx, int32_t* cu_ret, hipStream_t s);
 hipError_t launch_compact(int batch, int B, const uint8_t* keep, int32_t* idx,
                           int32_t* cu_ret, hipStream_t s);
 

@@ -77,14 +77,15 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[2], int lane) {
   }
 }
 
-// One wavefront per sequence. Lane l holds block positions l and l + 64.
+// Head mean, MaxPool1D, delta and top-K of sequence b by one wavefront
+// (lane l holds block positions l and l + 64). Writes dI and keep; returns
+// in `flag` the keep flag of positions lane and lane + 64, and kb.
 template <int NS>
-__global__ void __launch_bounds__(64) delta_topk_kernel(
-    int B, int Hq, int radius, const float* __restrict__ imp0,
+__device__ __forceinline__ void delta_topk_wave(
+    int b, int B, int Hq, int radius, const float* __restrict__ imp0,
     const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
-    uint8_t* __restrict__ keep, float* __restrict__ dI) {
-  __shared__ float mean[2][128];
-  const int b = blockIdx.x;
+    uint8_t* __restrict__ keep, float* __restrict__ dI, float (*mean)[128],
+    uint8_t* flags, int& kb_out) {
   const int lane = threadIdx.x;
   const float inv_h = 1.0f / (float)Hq;
   const float* i0 = imp0 + (size_t)b * Hq * B;
@@ -127,8 +128,66 @@ __global__ void __launch_bounds__(64) delta_topk_kernel(
     const int p = lane + 64 * s;  // rank in descending order
     if (key[s] != 0) {
       const int j = (int)(0xFFFFFFFFu - (uint32_t)key[s]);
-      keep[(size_t)b * B + j] = p < kb ? 1 : 0;
+      const uint8_t k = p < kb ? 1 : 0;
+      keep[(size_t)b * B + j] = k;
+      if (flags != nullptr) flags[j] = k;
     }
+  }
+  kb_out = kb;
+}
+
+// One wavefront per sequence.
+template <int NS>
+__global__ void __launch_bounds__(64) delta_topk_kernel(
+    int B, int Hq, int radius, const float* __restrict__ imp0,
+    const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
+    uint8_t* __restrict__ keep, float* __restrict__ dI) {
+  __shared__ float mean[2][128];
+  int kb;
+  delta_topk_wave<NS>(blockIdx.x, B, Hq, radius, imp0, imp1, k_keep, keep, dI,
+                      mean, nullptr, kb);
+}
+
+// Delta/top-K and compaction in one launch, one wavefront per sequence.
+// The offset of sequence b is the sum of the clamped budgets of the
+// sequences before it (top-K keeps exactly that many), summed by the wave
+// itself; kept positions are ranked in ascending order with a ballot and
+// mbcnt over the keep flags.
+template <int NS>
+__global__ void __launch_bounds__(64) select_kernel(
+    int batch, int B, int Hq, int radius, const float* __restrict__ imp0,
+    const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
+    uint8_t* __restrict__ keep, float* __restrict__ dI,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cu_ret) {
+  __shared__ float mean[2][128];
+  __shared__ uint8_t flags[128];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  int off = 0;
+  for (int c = 0; c < b; c += 64) {
+    const int i = c + lane;
+    if (i < b) off += min(max(k_keep[i], 0), B);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
+  int kb;
+  delta_topk_wave<NS>(b, B, Hq, radius, imp0, imp1, k_keep, keep, dI, mean,
+                      flags, kb);
+  __syncthreads();
+  int base = off;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = lane + 64 * s;
+    const bool kept = j < B && flags[j] != 0;
+    const uint64_t m = __ballot(kept);
+    const int rank = __builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (kept) idx[base + rank] = b * B + j;
+    base += __popcll(m);
+  }
+  if (lane == 0) {
+    cu_ret[b] = off;
+    if (b == batch - 1) cu_ret[batch] = off + kb;
   }
 }
 
@@ -232,6 +291,20 @@ hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
   } else {
     hipLaunchKernelGGL(delta_topk_kernel<2>, dim3(batch), dim3(64), 0, s, B, Hq,
                        (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(int batch, int B, int Hq, int pool_k,
+                         const float* imp0, const float* imp1,
+                         const int32_t* k_keep, uint8_t* keep, float* dI,
+                         int32_t* idx, int32_t* cu_ret, hipStream_t s) {
+  if (B <= 64) {
+    hipLaunchKernelGGL(select_kernel<1>, dim3(batch), dim3(64), 0, s, batch, B, Hq,
+                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI, idx, cu_ret);
+  } else {
+    hipLaunchKernelGGL(select_kernel<2>, dim3(batch), dim3(64), 0, s, batch, B, Hq,
+                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI, idx, cu_ret);
   }
   return hipGetLastError();
 }

@@ -1,9 +1,12 @@
 """One importance + evict block-step through the libfocus entry points.
 
 Order of calls per step (one stream, no host synchronisation):
+  focus_schedule (longest-prefix-first visiting order, shared by the
+  attention calls of the step);
   focus_block_attn_importance on layer 0, then on layer 1;
-  focus_delta_topk (head mean, MaxPool1D, delta, top-K);
-  focus_compact (retained indices and per-sequence offsets);
+  focus_select (head mean, MaxPool1D, delta, top-K and the retained
+  indices with per-sequence offsets, in one launch), or the same as two
+  calls, focus_delta_topk then focus_compact (fused=False);
   focus_retained_attn once per further layer.
 This module only allocates the output buffers (torch device memory) and
 calls the binding; it computes nothing itself.
@@ -19,7 +22,7 @@ import torch
 from . import (dtype_code, focus_block_attn_importance,
                focus_block_attn_importance_workspace, focus_compact,
                focus_delta_topk, focus_retained_attn,
-               focus_retained_attn_workspace)
+               focus_retained_attn_workspace, focus_schedule, focus_select)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -46,8 +49,9 @@ class FocusStep:
 
     def __init__(self, dims: Dims, cu_prefix_host: Sequence[int],
                  k_keep_host: Sequence[int], n_further: int = 0,
-                 device="cuda", with_lse: bool = False):
+                 device="cuda", with_lse: bool = False, fused: bool = True):
         self.dims = dims
+        self.fused = fused
         dv = torch.device(device)
         n, blk, hq, d = dims.batch, dims.block, dims.hq, dims.head_dim
         cu = np.asarray(cu_prefix_host, dtype=np.int64)
@@ -67,6 +71,7 @@ class FocusStep:
         self.idx = torch.empty((max(n * blk, 1),), device=dv,
                                dtype=torch.int32)
         self.cu_ret = torch.empty((n + 1,), device=dv, dtype=torch.int32)
+        self.order = torch.empty((n,), device=dv, dtype=torch.int32)
         self.ret_out = [torch.empty((max(self.n_ret, 1), hq, d), device=dv,
                                     dtype=dims.dtype)
                         for _ in range(n_further)]
@@ -79,18 +84,26 @@ class FocusStep:
                    if self.ws_bytes else None)
 
     # -- single calls -----------------------------------------------------
+    def schedule(self, stream=None) -> None:
+        focus_schedule(self.dims.batch, self.cu_prefix, self.order, stream)
+
     def block_attn(self, layer: Dict[str, torch.Tensor], which: int,
                    stream=None) -> None:
         dm = self.dims
         focus_block_attn_importance(
             dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
             dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
-            layer["k_cache"], layer["v_cache"], self.cu_prefix,
+            layer["k_cache"], layer["v_cache"], self.cu_prefix, self.order,
             self.max_prefix, self.out[which], self.imp[which],
             self.lse[which], self.ws, self.ws_bytes, stream)
 
     def select(self, stream=None) -> None:
         dm = self.dims
+        if self.fused:
+            focus_select(dm.batch, dm.block, dm.hq, dm.pool_k, self.imp[0],
+                         self.imp[1], self.k_keep, self.keep, self.dI,
+                         self.idx, self.cu_ret, stream)
+            return
         focus_delta_topk(dm.batch, dm.block, dm.hq, dm.pool_k, self.imp[0],
                          self.imp[1], self.k_keep, self.keep, self.dI, stream)
         focus_compact(dm.batch, dm.block, self.keep, self.idx, self.cu_ret,
@@ -103,7 +116,7 @@ class FocusStep:
             dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
             dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
             self.idx, self.cu_ret, self.n_ret, self.max_ret,
-            layer["k_cache"], layer["v_cache"], self.cu_prefix,
+            layer["k_cache"], layer["v_cache"], self.cu_prefix, self.order,
             self.max_prefix, self.ret_out[which], self.ws, self.ws_bytes,
             stream)
 
@@ -111,6 +124,7 @@ class FocusStep:
     def run(self, layers: List[Dict[str, torch.Tensor]], stream=None) -> None:
         """layers[0], layers[1]: importance layers; layers[2:]: further
         layers run on the retained tokens."""
+        self.schedule(stream)
         self.block_attn(layers[0], 0, stream)
         self.block_attn(layers[1], 1, stream)
         self.select(stream)

@@ -60,6 +60,23 @@ const char* focus_status_string(focus_status s);
  * thread ("" if none). Valid until the next libfocus call on the thread. */
 const char* focus_last_error(void);
 
+/*
+ * Visiting order of the sequences for the attention calls of one step:
+ * longest prefix first, equal lengths by lower index. The attention work of
+ * a sequence grows with its prefix length, and visiting the long ones
+ * first keeps every compute unit streaming until the end of the launch.
+ * The pages' scheduler prepares per-sequence metadata for each step
+ * before the kernels run (Pith page, scheduler appendix fragments); this
+ * call is that step for the work order, done on the device from cu_prefix.
+ *
+ *  cu_prefix   device int32 [batch+1] as in focus_block_attn_importance.
+ *  order       device int32 [batch] output, a permutation of 0..batch-1.
+ * Batches above 8192 keep their natural order.
+ * Errors: INVALID_ARG (batch < 1, NULL pointer), HIP.
+ */
+focus_status focus_schedule(int batch, const int32_t* cu_prefix, int32_t* order,
+                            void* stream);
+
 /* Workspace bytes that focus_block_attn_importance needs for these sizes.
  * Writes *bytes; never fails for valid sizes. */
 focus_status focus_block_attn_importance_workspace(
@@ -91,12 +108,18 @@ focus_status focus_block_attn_importance_workspace(
  *  k_cache,v_cache [cu_prefix[batch], Hkv, d]  packed prefix KV, sequence
  *              after sequence
  *  cu_prefix   device int32 [batch+1], cu_prefix[0] = 0, non-decreasing.
+ *  order       device int32 [batch]: the order in which sequences are
+ *              visited, a permutation of 0..batch-1 (focus_schedule writes
+ *              the longest-prefix-first one). Results do not depend on it;
+ *              only the run time does. Entries are clamped to [0, batch).
+ *              NULL: the call writes that order into the workspace first
+ *              (one extra kernel launch).
  *  max_prefix  host promise: max_b P_b (sizes the launch).
  *  out         [batch*B, Hq, d] attention output (type dt).
  *  imp         float32 [batch, Hq, B] importance of the block columns.
  *  lse         float32 [batch, Hq, B] natural-log row lse, or NULL.
- *  workspace   device scratch of at least the queried size (may be NULL if
- *              that size is 0); its contents on entry do not matter.
+ *  workspace   device scratch of at least the queried size, needed only
+ *              when order is NULL; its contents on entry do not matter.
  * Errors: INVALID_ARG (null required pointer, batch < 1, B not in [1,128],
  * Hq or Hkv < 1, max_prefix < 0, misaligned pointer), UNSUPPORTED (d not
  * 64/128, bad dt, Hq % Hkv != 0), WORKSPACE, HIP.
@@ -105,7 +128,7 @@ focus_status focus_block_attn_importance(
     focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
     const void* q, const void* k_blk, const void* v_blk,
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
-    int max_prefix, void* out, float* imp, float* lse,
+    const int32_t* order, int max_prefix, void* out, float* imp, float* lse,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -148,6 +171,26 @@ focus_status focus_delta_topk(
 focus_status focus_compact(int batch, int B, const uint8_t* keep,
                            int32_t* idx, int32_t* cu_ret, void* stream);
 
+/*
+ * focus_delta_topk followed by focus_compact, in one launch.
+ *
+ * Same definitions and outputs as those two calls (keep, dI, idx, cu_ret
+ * are bit-identical to calling them in sequence): the importance delta and
+ * top-K of the Pith page, "What carries the argument", then the retained
+ * tokens' index list for the remaining layers ("The pith"). Each sequence's
+ * offset in idx is the sum of min(max(K_b', 0), B) over the sequences
+ * before it, which is what top-K keeps. One kernel instead of two on the
+ * per-step path; the per-sequence offset sum costs O(batch) per sequence.
+ *
+ *  idx     int32, capacity batch*B; cu_ret int32 [batch+1]; others as in
+ *          focus_delta_topk. dI may be NULL.
+ * Errors: as focus_delta_topk, plus INVALID_ARG for NULL idx / cu_ret.
+ */
+focus_status focus_select(int batch, int B, int Hq, int pool_k,
+                          const float* imp0, const float* imp1,
+                          const int32_t* k_keep, uint8_t* keep, float* dI,
+                          int32_t* idx, int32_t* cu_ret, void* stream);
+
 /* Workspace bytes that focus_retained_attn needs for these sizes. */
 focus_status focus_retained_attn_workspace(
     int batch, int Hq, int Hkv, int d, int max_prefix, int n_ret,
@@ -164,8 +207,8 @@ focus_status focus_retained_attn_workspace(
  *  idx, cu_ret from focus_compact (device).
  *  n_ret       host promise: cu_ret[batch] (rows of out).
  *  max_ret     host promise: max_b (cu_ret[b+1] - cu_ret[b]), <= B.
- *  k_cache,v_cache,cu_prefix,max_prefix  as in focus_block_attn_importance,
- *              for this layer.
+ *  k_cache,v_cache,cu_prefix,order,max_prefix  as in
+ *              focus_block_attn_importance, for this layer.
  *  out         [n_ret, Hq, d] (type dt), row r is the query of idx[r].
  * n_ret == 0 enqueues nothing and returns FOCUS_OK.
  * Errors: as focus_block_attn_importance, plus INVALID_ARG for n_ret < 0 or
@@ -176,8 +219,8 @@ focus_status focus_retained_attn(
     const void* q_src, const void* k_src, const void* v_src,
     const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
-    int max_prefix, void* out, void* workspace, size_t workspace_bytes,
-    void* stream);
+    const int32_t* order, int max_prefix, void* out, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(F.lib, name), name
         assert callable(getattr(F, name)), name
@@ -45,14 +45,14 @@ def test_version_and_status_strings():
 def _attn(**kw):
     a = dict(dt=1, batch=2, B=32, Hq=32, Hkv=8, d=128, scale=0.0, q=FAKE,
              k_blk=FAKE, v_blk=FAKE, k_cache=FAKE, v_cache=FAKE,
-             cu_prefix=FAKE, max_prefix=16, out=FAKE, imp=FAKE, lse=None,
-             ws=None, ws_bytes=0, stream=None)
+             cu_prefix=FAKE, order=None, max_prefix=16, out=FAKE, imp=FAKE,
+             lse=None, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return F.lib.focus_block_attn_importance(
         a["dt"], a["batch"], a["B"], a["Hq"], a["Hkv"], a["d"], a["scale"],
         a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"],
-        a["cu_prefix"], a["max_prefix"], a["out"], a["imp"], a["lse"],
-        a["ws"], a["ws_bytes"], a["stream"])
+        a["cu_prefix"], a["order"], a["max_prefix"], a["out"], a["imp"],
+        a["lse"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,6 +71,8 @@ def _attn(**kw):
     (dict(k_cache=None), F.FOCUS_ERR_INVALID_ARG),
     (dict(q=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),
     (dict(lse=FAKE + 8), F.FOCUS_ERR_INVALID_ARG),
+    (dict(order=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=0), F.FOCUS_ERR_WORKSPACE),
 ])
 def test_block_attention_rejects_bad_arguments(kw, code):
     assert _attn(**kw) == code
@@ -112,16 +114,33 @@ def test_compact_rejects_bad_arguments(args, code):
     assert F.lib.focus_compact(*args) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(B=129), F.FOCUS_ERR_INVALID_ARG),
+    (dict(pool_k=2), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(idx=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(cu_ret=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(imp0=FAKE + 2), F.FOCUS_ERR_INVALID_ARG),
+])
+def test_select_rejects_bad_arguments(kw, code):
+    a = dict(batch=2, B=32, Hq=32, pool_k=3, imp0=FAKE, imp1=FAKE,
+             k_keep=FAKE, keep=FAKE, dI=None, idx=FAKE, cu_ret=FAKE)
+    a.update(kw)
+    assert F.lib.focus_select(a["batch"], a["B"], a["Hq"], a["pool_k"],
+                              a["imp0"], a["imp1"], a["k_keep"], a["keep"],
+                              a["dI"], a["idx"], a["cu_ret"], None) == code
+
+
 def _ret(**kw):
     a = dict(dt=1, batch=2, B=32, Hq=32, Hkv=8, d=128, scale=0.0, q=FAKE,
              k=FAKE, v=FAKE, idx=FAKE, cu_ret=FAKE, n_ret=10, max_ret=5,
-             k_cache=FAKE, v_cache=FAKE, cu_prefix=FAKE, max_prefix=16,
-             out=FAKE, ws=None, ws_bytes=0, stream=None)
+             k_cache=FAKE, v_cache=FAKE, cu_prefix=FAKE, order=None,
+             max_prefix=16, out=FAKE, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return F.lib.focus_retained_attn(
         a["dt"], a["batch"], a["B"], a["Hq"], a["Hkv"], a["d"], a["scale"],
         a["q"], a["k"], a["v"], a["idx"], a["cu_ret"], a["n_ret"],
-        a["max_ret"], a["k_cache"], a["v_cache"], a["cu_prefix"],
+        a["max_ret"], a["k_cache"], a["v_cache"], a["cu_prefix"], a["order"],
         a["max_prefix"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -137,6 +156,15 @@ def _ret(**kw):
 ])
 def test_retained_attention_arguments(kw, code):
     assert _ret(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, FAKE, FAKE, None), F.FOCUS_ERR_INVALID_ARG),
+    ((4, None, FAKE, None), F.FOCUS_ERR_INVALID_ARG),
+    ((4, FAKE, None, None), F.FOCUS_ERR_INVALID_ARG),
+])
+def test_schedule_rejects_bad_arguments(args, code):
+    assert F.lib.focus_schedule(*args) == code
 
 
 def test_workspace_queries():

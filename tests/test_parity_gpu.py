@@ -88,6 +88,35 @@ def test_retained_with_full_budget_equals_block_attention():
     assert err <= 1e-6
 
 
+def test_visiting_order_does_not_change_results():
+    """With order=NULL (the call schedules itself), with focus_schedule's
+    order, and with the reversed order, every output is bitwise equal."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=12)
+    log("[parity] visiting order independence")
+    inp = workloads.make_inputs(cfg, 4, n_layers=3)
+    lay = parity.to_device(inp)
+    step, r1 = parity.run_gpu(inp, layers_dev=lay)
+    order = step.order.cpu().numpy()
+    plen = inp.meta.prefix_lens
+    assert sorted(order.tolist()) == list(range(12))
+    assert all(plen[order[i]] >= plen[order[i + 1]] for i in range(11))
+    outs = []
+    for variant in ("none", "reversed"):
+        o = [torch.empty_like(step.out[0]), torch.empty_like(step.imp[0])]
+        ordr = None if variant == "none" else torch.flip(step.order, [0]).contiguous()
+        dm = step.dims
+        F.focus_block_attn_importance(
+            F.FOCUS_BF16, dm.batch, dm.block, dm.hq, dm.hkv, dm.head_dim, 0.0,
+            lay[0]["q"], lay[0]["k_blk"], lay[0]["v_blk"], lay[0]["k_cache"],
+            lay[0]["v_cache"], step.cu_prefix, ordr, step.max_prefix, o[0], o[1],
+            None, step.ws, step.ws_bytes)
+        torch.cuda.synchronize()
+        outs.append(o)
+    for o in outs:
+        assert torch.equal(o[0], step.out[0]) and torch.equal(o[1], step.imp[0])
+
+
 def test_deterministic_bitwise():
     cfg = workloads.scaled(workloads.get("c3"), batch=8)
     log("[parity] determinism")
@@ -100,6 +129,36 @@ def test_deterministic_bitwise():
     for k in ("out", "imp", "lse", "ret"):
         for a, b in zip(r1[k], r2[k]):
             assert np.array_equal(a, b), k
+
+
+@pytest.mark.parametrize("over,plens,kk", [
+    (dict(), None, None),
+    (dict(block=128, pool_k=5), [100, 0, 3000], [32, 0, 128]),
+    (dict(block=7), [5, 9, 1, 0], [0, 7, 3, 1]),
+])
+def test_fused_select_equals_two_calls(over, plens, kk):
+    """focus_select must be bit-identical to focus_delta_topk followed by
+    focus_compact (keep, dI, idx, cu_ret)."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 40,
+                           **over)
+    log(f"[parity] fused select B={cfg.block} N={cfg.batch}")
+    inp = workloads.make_inputs(cfg, 9, n_layers=2, prefix_lens=plens, k_keep=kk)
+    s1, r1 = parity.run_gpu(inp)
+    step = s1
+    keep2 = torch.zeros_like(step.keep)
+    dI2 = torch.zeros_like(step.dI)
+    idx2 = torch.full_like(step.idx, -7)
+    cu2 = torch.zeros_like(step.cu_ret)
+    dm = step.dims
+    F.focus_delta_topk(dm.batch, dm.block, dm.hq, dm.pool_k, step.imp[0], step.imp[1],
+                       step.k_keep, keep2, dI2)
+    F.focus_compact(dm.batch, dm.block, keep2, idx2, cu2)
+    torch.cuda.synchronize()
+    assert torch.equal(keep2.cpu(), torch.from_numpy(r1["keep"]))
+    assert torch.equal(dI2.cpu(), torch.from_numpy(r1["dI"]))
+    assert torch.equal(cu2.cpu(), torch.from_numpy(r1["cu_ret"]))
+    assert np.array_equal(idx2.cpu().numpy()[:step.n_ret], r1["idx"])
 
 
 def _full_size(name, cfg_name, seqs_pick, n_layers=None):
