@@ -124,11 +124,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
   const int n = lane & 31;    // query row inside the wave's 32-row block
   const int half = lane >> 5;
 
-  int wid = blockIdx.x;
-  const int hc = wid % a.n_hc;
-  wid /= a.n_hc;
-  const int g = wid % a.Hkv;
-  const int rank = wid / a.Hkv;
+  int item, hc;
+  attn_work_item(blockIdx.x, a.n_hc, &item, &hc);
+  if (item >= a.batch * a.Hkv) return;  // grid padding, uniform per block
+  const int g = item % a.Hkv;
+  const int rank = item / a.Hkv;
   const int b = a.order != nullptr ? min(max(a.order[rank], 0), a.batch - 1) : rank;
 
   const int p0 = a.cu_prefix[b];
@@ -422,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
 
 template <bool RET>
 hipError_t launch(Elem e, int d, int batch, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)batch * a.Hkv * a.n_hc);
+  const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc));
   const dim3 block(kThreads);
   if (e == Elem::BF16 && d == 128) {
     hipLaunchKernelGGL((attn_kernel<RET, __bf16, 128>), grid, block, 0, s, a);

@@ -135,11 +135,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   const int n = lane & 31;
   const int half = lane >> 5;
 
-  int wid = blockIdx.x;
-  const int hc = wid % a.n_hc;
-  wid /= a.n_hc;
-  const int g = wid % a.Hkv;
-  const int rank = wid / a.Hkv;
+  int item, hc;
+  attn_work_item(blockIdx.x, a.n_hc, &item, &hc);
+  if (item >= a.batch * a.Hkv) return;  // grid padding, uniform per block
+  const int g = item % a.Hkv;
+  const int rank = item / a.Hkv;
   const int b = a.order != nullptr ? min(max(a.order[rank], 0), a.batch - 1) : rank;
 
   const int p0 = a.cu_prefix[b];
@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
 
 template <bool RET>
 hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)batch * a.Hkv * a.n_hc), block(kThreads);
+  const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(kThreads);
   switch (nbt) {
     case 1: hipLaunchKernelGGL((attn_bf16_kernel<RET, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((attn_bf16_kernel<RET, 2>), grid, block, 0, s, a); break;

@@ -43,6 +43,26 @@ struct AttnArgs {
   float sl2;              // softmax scale * log2(e)
 };
 
+// Workgroups are dispatched to the 8 XCDs of an MI355X round-robin by
+// block index, and each XCD has its own L2. The attention grid therefore
+// keeps the n_hc query-head chunks of one (sequence, KV head) item -- which
+// all stream the same K/V -- on one XCD: item i goes to XCD i % 8, and its
+// chunks are consecutive in that XCD's dispatch order.
+constexpr int kXcds = 8;
+
+__host__ __device__ inline unsigned attn_grid_size(int items, int n_hc) {
+  return (unsigned)((items + kXcds - 1) / kXcds) * kXcds * (unsigned)n_hc;
+}
+
+// Decodes a block index into (item, chunk); item >= items marks padding.
+__device__ inline void attn_work_item(int blk, int n_hc, int* item, int* hc) {
+  const int x = blk % kXcds;
+  const int s = blk / kXcds;
+  const int q = s / n_hc;
+  *item = kXcds * q + x;
+  *hc = s - q * n_hc;
+}
+
 enum class Elem { F32 = 0, BF16 = 1 };
 
 // Launchers; return the launch status.
