@@ -61,6 +61,8 @@ focus_status check_attn_shape(const char* fn, int dt, int batch, int B,
     return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
   if (Hq < 1 || Hkv < 1)
     return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d / Hkv %d < 1", fn, Hq, Hkv);
+  if (Hq > focus::kMaxHeads)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d > %d", fn, Hq, focus::kMaxHeads);
   if (max_prefix < 0)
     return fail(FOCUS_ERR_INVALID_ARG, "%s: max_prefix %d < 0", fn, max_prefix);
   if (Hq % Hkv != 0)

@@ -20,9 +20,10 @@
 //    lazy rescale of O: the running max only moves (and O is only rescaled)
 //    when a row max grows by more than 2^8; the final O / l and lse are
 //    exact whatever max was used.
-//  * The block keys are processed first and their raw scores stay in
+//  * The block keys are processed last and their raw scores stay in
 //    registers, so the importance pass needs neither a reload nor a
-//    recompute once the final lse is known.
+//    recompute once the final lse is known (and those registers are free
+//    during the prefix stream).
 //  * Work items are visited longest prefix first (order from a one-block
 //    bitonic sort of the prefix lengths), the 8 KV heads of a sequence on
 //    neighbouring workgroups.
@@ -79,7 +80,10 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // (+2048 bytes), each read with ds_read_b64_tr_b16. The reads sit in one
 // asm block that also waits for them, so no output register is ever left
 // with a load in flight (and the compiler adds no wait of its own for the
-// direct-to-LDS loads that may still be landing in other ring stages).
+// direct-to-LDS loads that may still be landing in other ring stages). The
+// outputs are early-clobber: a read may land while a later read of the
+// block has not yet taken its address, so no output may share a register
+// with an address.
 #define FOCUS_TR8(OFF0, OFF1)                                                 \
   asm volatile(                                                               \
       "ds_read_b64_tr_b16 %0, %8 offset:" #OFF0 "\n\t"                        \
@@ -91,8 +95,8 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
       "ds_read_b64_tr_b16 %6, %11 offset:" #OFF0 "\n\t"                       \
       "ds_read_b64_tr_b16 %7, %11 offset:" #OFF1 "\n\t"                       \
       "s_waitcnt lgkmcnt(0)"                                                  \
-      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]), "=v"(f[4]),           \
-        "=v"(f[5]), "=v"(f[6]), "=v"(f[7])                                    \
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]),      \
+        "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7])                                 \
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3)                                    \
       : "memory")
 
@@ -169,19 +173,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   const int npt = (plen + TK - 1) / TK;
   const int nt = nbt + npt;
 
-  // Block rows this lane loads (gathered in retained mode), resolved up
-  // front so that no index load sits between the streaming loads.
-  int brow[NBT][2];
+  // Retained mode: the block rows this lane loads (gathered through idx),
+  // resolved up front so that no index load sits between the streaming
+  // loads. Block mode computes them from rbase.
+  int brow[RET ? NBT : 1][2];
+  if constexpr (RET) {
 #pragma unroll
-  for (int bt = 0; bt < NBT; ++bt) {
+    for (int bt = 0; bt < NBT; ++bt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int j = bt * TK + lrow0 + 4 * i;
-      j = min(j, nq - 1);  // rows past the end repeat the last row (masked)
-      if constexpr (RET) {
+      for (int i = 0; i < 2; ++i) {
+        // rows past the end repeat the last row (masked)
+        const int j = min(bt * TK + lrow0 + 4 * i, nq - 1);
         brow[bt][i] = bt < nbt ? a.idx[rbase + j] : 0;
-      } else {
-        brow[bt][i] = rbase + j;
       }
     }
   }
@@ -193,33 +196,60 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   const size_t rowstride = (size_t)a.Hkv * ROWB;  // bytes between tokens
   const size_t goff = (size_t)g * ROWB;
 
+  // Byte offsets of the two rows this lane loads in a prefix tile, relative
+  // to the tile's first token: full tiles add one scalar base per tile.
+  // (32 rows of at most kMaxHeads heads stay below 2^32 bytes.)
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int lr = lrow0 + 4 * i;
+    const uint32_t rb = (uint32_t)(lr * rowstride + goff);
+    koff[i] = rb + ((pchunk ^ (lr & 15)) << 4);
+    voff[i] = rb + ((pchunk ^ ((lr & 3) << 2)) << 4);
+  }
+
+  // Tiles 0 .. npt-1 are the prefix, npt .. nt-1 the block.
   auto issue_tile = [&](int t) {
     char* st = smem + (t % NSTAGE) * STAGEB;
+    if ((t + 1) * TK <= plen) {
+      // full prefix tile
+      const size_t tb = (size_t)(p0 + t * TK) * rowstride;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        char* dst = st + (2 * wave + i) * 1024;
+        dma16(kc + tb + koff[i], dst);
+        dma16(vc + tb + voff[i], dst + TILEB);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int lr = lrow0 + 4 * i;          // row inside the tile
-      size_t row;
+      int row;
       const char *ksrc, *vsrc;
-      if (t < nbt) {
-        int rr = 0;
-#pragma unroll
-        for (int bt = 0; bt < NBT; ++bt)
-          if (bt == t) rr = brow[bt][i];
-        row = (size_t)rr;
-        ksrc = kb;
-        vsrc = vb;
-      } else {
-        const int pt = t - nbt;
-        row = (size_t)(p0 + min(pt * TK + lr, plen - 1));
+      if (t < npt) {
+        // last, partial prefix tile: rows past the end repeat the last row
+        row = p0 + min(t * TK + lr, plen - 1);
         ksrc = kc;
         vsrc = vc;
+      } else {
+        const int bt = t - npt;
+        if constexpr (RET) {
+          row = 0;
+#pragma unroll
+          for (int k = 0; k < NBT; ++k)
+            if (k == bt) row = brow[k][i];
+        } else {
+          row = rbase + min(bt * TK + lr, nq - 1);
+        }
+        ksrc = kb;
+        vsrc = vb;
       }
-      const size_t base = row * rowstride + goff;
-      const int kch = pchunk ^ (lr & 15);
-      const int vch = pchunk ^ ((lr & 3) << 2);
+      // koff/voff hold lr * rowstride; take it back out in integers
+      const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
       char* dst = st + (2 * wave + i) * 1024;
-      dma16(ksrc + base + kch * 16, dst);
-      dma16(vsrc + base + vch * 16, dst + TILEB);
+      dma16(ksrc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
+      dma16(vsrc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
     }
   };
 
@@ -278,27 +308,27 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
     return acc;
   };
   auto tile_cnt = [&](int t) {
-    return t < nbt ? min(TK, nq - t * TK) : min(TK, plen - (t - nbt) * TK);
+    return t < npt ? min(TK, plen - t * TK) : min(TK, nq - (t - npt) * TK);
   };
 
-  // Tile 0 must be in LDS before its scores; tiles 1.. may still land.
-  wait_and_barrier(4 * (min(nt, NSTAGE - 1) - 1));
-  f32x16 s_cur = {};
-  if (wave_on) s_cur = qk(0);
+  // V^T fragment offsets inside a V tile, one per head-dim tile.
+  uint32_t va_off[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    va_off[dt] = vrow_base * ROWB + (((4 * dt + vchunk_base) ^ (4 * ve)) << 4) + vbyte;
 
-  // Software pipeline: iteration t computes the scores of tile t + 1 on
-  // the matrix cores while the vector units run the softmax of tile t and
-  // its P V product. Tiles t and t + 1 are resident at the top of the
-  // iteration; the ring slot of tile t - 1 is then refilled with tile t + 3.
-  for (int t = 0; t < nt; ++t) {
+  // One tile of the software pipeline: the scores of tile t + 1 are issued
+  // on the matrix cores (into s_nxt) while the vector units run the softmax
+  // of tile t (s_cur) and its P V product. Tiles t and t + 1 are resident at
+  // the top; the ring slot of tile t - 1 is then refilled with tile t + 3.
+  // cap, when given, receives the masked raw scores of a block tile.
+  auto tile_step = [&](int t, f32x16& s_cur, f32x16& s_nxt, f32x16* cap) {
     wait_and_barrier(t + 2 < nt ? 4 : 0);
     if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
-    if (!wave_on) continue;
+    if (!wave_on) return;
+    if (t + 1 < nt) s_nxt = qk(t + 1);
 
-    f32x16 s_next = {};
-    if (t + 1 < nt) s_next = qk(t + 1);
-
-    f32x16 s = s_cur;
+    f32x16& s = s_cur;
     const int cnt = tile_cnt(t);
     if (cnt < TK) {
 #pragma unroll
@@ -307,16 +337,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
         if (key >= cnt) s[v] = -INFINITY;
       }
     }
-    if constexpr (!RET) {
-#pragma unroll
-      for (int bt = 0; bt < NBT; ++bt)
-        if (bt == t) sblk[bt] = s;
-    }
-    const float m4a = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    const float m4b = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
-    const float m4c = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
-    const float m4d = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
-    const float mx = pair_max(fmaxf(fmaxf(m4a, m4b), fmaxf(m4c, m4d))) * c;
+    if (cap != nullptr) *cap = s;
+    const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    const float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
+    const float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float mm = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
+    const float mx = pair_max(mm) * c;
     if (__any(mx > mrun + kLazy)) {
       const float mnew = fmaxf(mrun, mx);
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
@@ -333,32 +361,50 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
     for (int v = 0; v < 8; ++v) q8[v] = s[2 * v] + s[2 * v + 1];
     lsum += ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
 
-    {
-      const char* vs = smem + (t % NSTAGE) * STAGEB + TILEB;
-      // V^T fragment addresses for this stage, one per head-dim tile.
-      uint32_t va[4];
+    const uint32_t vbase = lds_addr(smem + (t % NSTAGE) * STAGEB + TILEB);
+    u32x2v f0[8], f1[8];
+    v_frags<0>(vbase + va_off[0], vbase + va_off[1], vbase + va_off[2],
+               vbase + va_off[3], f0);
+    bf16x8 pb;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        va[dt] = lds_addr(vs) + vrow_base * ROWB +
-                 (((4 * dt + vchunk_base) ^ (4 * ve)) << 4) + vbyte;
-      u32x2v f0[8], f1[8];
-      v_frags<0>(va[0], va[1], va[2], va[3], f0);
-      bf16x8 pb;
+    for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[e]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[e]);
+    for (int dt = 0; dt < 4; ++dt)
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          cat8(f0[2 * dt], f0[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
+    v_frags<1>(vbase + va_off[0], vbase + va_off[1], vbase + va_off[2],
+               vbase + va_off[3], f1);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            cat8(f0[2 * dt], f0[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
-      v_frags<1>(va[0], va[1], va[2], va[3], f1);
+    for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 + e]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 + e]);
+    for (int dt = 0; dt < 4; ++dt)
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          cat8(f1[2 * dt], f1[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
+  };
+
+  // Tile 0 must be in LDS before its scores; tiles 1.. may still land.
+  wait_and_barrier(4 * (min(nt, NSTAGE - 1) - 1));
+  f32x16 sa = {}, sb = {};
+  if (wave_on) sa = qk(0);
+  // Prefix tiles two at a time, so that the score registers alternate
+  // instead of being copied between iterations; then the block tiles,
+  // unrolled, each keeping its raw scores in registers of its own for the
+  // importance pass (live only from here on).
+  for (int t = 0; t < npt; t += 2) {
+    tile_step(t, sa, sb, nullptr);
+    if (t + 1 < npt) tile_step(t + 1, sb, sa, nullptr);
+  }
+  if (npt & 1) sa = sb;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            cat8(f1[2 * dt], f1[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
+  for (int bt = 0; bt < NBT; ++bt) {
+    if (bt < nbt) {
+      f32x16* cap = nullptr;
+      if constexpr (!RET) cap = &sblk[bt];
+      if (bt & 1)
+        tile_step(npt + bt, sb, sa, cap);
+      else
+        tile_step(npt + bt, sa, sb, cap);
     }
-    s_cur = s_next;
   }
 
   const float ltot = pair_sum(lsum);

@@ -48,6 +48,9 @@ struct AttnArgs {
 // keeps the n_hc query-head chunks of one (sequence, KV head) item -- which
 // all stream the same K/V -- on one XCD: item i goes to XCD i % 8, and its
 // chunks are consecutive in that XCD's dispatch order.
+// Heads per token are bounded so that a 32-token tile of one KV head spans
+// less than 4 GiB and in-tile byte offsets fit 32 bits.
+constexpr int kMaxHeads = 4096;
 constexpr int kXcds = 8;
 
 __host__ __device__ inline unsigned attn_grid_size(int items, int n_hc) {
