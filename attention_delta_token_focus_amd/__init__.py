@@ -148,10 +148,10 @@ def focus_block_attn_importance(dt, batch, B, Hq, Hkv, d, scale, q, k_blk,
                                 stream=None) -> None:
     _check(lib.focus_block_attn_importance(
         dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
-        _ptr(q, "q"), _ptr(k_blk, "k_blk"), _ptr(v_blk, "v_blk"),
+        _ptr(q, "q"), _ptr(k_blk, "k_blk"), _ptr(v_blk, "v_blk", True),
         _ptr(k_cache, "k_cache", True), _ptr(v_cache, "v_cache", True),
         _ptr(cu_prefix, "cu_prefix"), _ptr(order, "order", True),
-        max_prefix, _ptr(out, "out"),
+        max_prefix, _ptr(out, "out", True),
         _ptr(imp, "imp"), _ptr(lse, "lse", True),
         _ptr(workspace, "workspace", True), workspace_bytes,
         _stream(stream)))

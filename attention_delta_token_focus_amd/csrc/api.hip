@@ -162,16 +162,17 @@ focus_status focus_block_attn_importance(
     if (st != FOCUS_OK) return st;
     REQUIRE_PTR(q);
     REQUIRE_PTR(k_blk);
-    REQUIRE_PTR(v_blk);
     REQUIRE_PTR(cu_prefix);
-    REQUIRE_PTR(out);
     REQUIRE_PTR(imp);
+    OPTIONAL_PTR(out);
     OPTIONAL_PTR(lse);
     OPTIONAL_PTR(order);
     OPTIONAL_PTR(workspace);
+    // out == NULL: importance (and lse) only; the values are not read.
+    if (out != nullptr) REQUIRE_PTR(v_blk);
     if (max_prefix > 0) {
       REQUIRE_PTR(k_cache);
-      REQUIRE_PTR(v_cache);
+      if (out != nullptr) REQUIRE_PTR(v_cache);
     }
     size_t need = 0;
     st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);

@@ -264,9 +264,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
   float mrun = -INFINITY;  // running row max, log2 domain
   float lsum = 0.f;        // this lane's share of the row sum
 
-  load_tile(0, true);
-  store_tile(0, true);
-  if (nt > 1) load_tile(1, true);
+  // Importance only (block mode with out = NULL): no V, no P V.
+  const bool wo = a.out != nullptr;
+  load_tile(0, wo);
+  store_tile(0, wo);
+  if (nt > 1) load_tile(1, wo);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
@@ -308,6 +310,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
           reinterpret_cast<const T*>(smem + 2 * G::KBUF + buf * G::VBUF);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        if (!wo) break;
 #pragma unroll
         for (int st = 0; st < PVS; ++st) {
           frag pb;
@@ -337,8 +340,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
         }
       }
     }
-    if (t + 1 < nt) store_tile(buf ^ 1, true);
-    if (t + 2 < nt) load_tile(t + 2, true);
+    if (t + 1 < nt) store_tile(buf ^ 1, wo);
+    if (t + 2 < nt) load_tile(t + 2, wo);
     __syncthreads();
   }
 
@@ -351,6 +354,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
     T* op = static_cast<T*>(a.out) + ((size_t)(rbase + qi) * a.Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      if (!wo) break;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = dt * 32 + 8 * q4 + 4 * half;

@@ -37,10 +37,10 @@ constexpr int NSTAGE = 4;       // ring depth
 constexpr int D = 128;
 constexpr int ROWB = D * 2;     // bytes per key row (256)
 constexpr int TILEB = TK * ROWB;        // 8 KB per K or V tile
-constexpr int STAGEB = 2 * TILEB;       // K + V
 constexpr int PPITCH = TK + 4;          // fp32 probability row pitch
-constexpr int SMEM = NSTAGE * STAGEB;   // 64 KB
-static_assert(kRowsPerWG * PPITCH * 4 <= SMEM, "pass-2 buffer fits the ring");
+// One ring stage holds a K tile and, when O is produced, a V tile.
+template <bool WO> constexpr int stage_bytes() { return WO ? 2 * TILEB : TILEB; }
+static_assert(kRowsPerWG * PPITCH * 4 <= NSTAGE * TILEB, "pass-2 buffer fits the ring");
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before O is rescaled
 
@@ -57,13 +57,15 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 }
 
 // Wait until at most `n` of this wave's vector-memory operations are
-// outstanding (n in {0, 4, 8}), then barrier. The memory clobber keeps the
-// compiler from moving LDS accesses across it.
+// outstanding (n in {0, 2, 4, 8}), then barrier. The memory clobber keeps
+// the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void wait_and_barrier(int n) {
   if (n >= 8) {
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else if (n >= 4) {
     asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else if (n >= 2) {
+    asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
@@ -129,8 +131,14 @@ __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-template <bool RET, int NBT>
-__global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a) {
+// WO: O is produced. Without it (importance only: block mode with out =
+// NULL) no V is loaded and no P V product is formed; the K-only ring is half
+// the size and three workgroups share a CU.
+template <bool RET, int NBT, bool WO>
+__global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const AttnArgs a) {
+  constexpr int STAGEB = stage_bytes<WO>();
+  constexpr int SMEM = NSTAGE * STAGEB;
+  constexpr int OPS = WO ? 4 : 2;  // loads per wave per tile
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -218,7 +226,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
       for (int i = 0; i < 2; ++i) {
         char* dst = st + (2 * wave + i) * 1024;
         dma16(kc + tb + koff[i], dst);
-        dma16(vc + tb + voff[i], dst + TILEB);
+        if constexpr (WO) dma16(vc + tb + voff[i], dst + TILEB);
       }
       return;
     }
@@ -249,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
       const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
       char* dst = st + (2 * wave + i) * 1024;
       dma16(ksrc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
-      dma16(vsrc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
+      if constexpr (WO) dma16(vsrc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
     }
   };
 
@@ -323,7 +331,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   // the top; the ring slot of tile t - 1 is then refilled with tile t + 3.
   // cap, when given, receives the masked raw scores of a block tile.
   auto tile_step = [&](int t, f32x16& s_cur, f32x16& s_nxt, f32x16* cap) {
-    wait_and_barrier(t + 2 < nt ? 4 : 0);
+    wait_and_barrier(t + 2 < nt ? OPS : 0);
     if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
     if (!wave_on) return;
     if (t + 1 < nt) s_nxt = qk(t + 1);
@@ -350,8 +358,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       mrun = mnew;
       lsum *= alpha;
+      if constexpr (WO) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+      }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v)
@@ -360,6 +370,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
 #pragma unroll
     for (int v = 0; v < 8; ++v) q8[v] = s[2 * v] + s[2 * v + 1];
     lsum += ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
+    if constexpr (!WO) return;
 
     const uint32_t vbase = lds_addr(smem + (t % NSTAGE) * STAGEB + TILEB);
     u32x2v f0[8], f1[8];
@@ -383,7 +394,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   };
 
   // Tile 0 must be in LDS before its scores; tiles 1.. may still land.
-  wait_and_barrier(4 * (min(nt, NSTAGE - 1) - 1));
+  wait_and_barrier(OPS * (min(nt, NSTAGE - 1) - 1));
   f32x16 sa = {}, sb = {};
   if (wave_on) sa = qk(0);
   // Prefix tiles two at a time, so that the score registers alternate
@@ -411,16 +422,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(const AttnArgs a
   const float lse2 = mrun + log2f(ltot);
 
   if (wave_on && row_ok) {
-    const float inv = 1.0f / ltot;
-    __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)(rbase + qi) * a.Hq + h) * D;
+    if constexpr (WO) {
+      const float inv = 1.0f / ltot;
+      __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)(rbase + qi) * a.Hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 o;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * half) = o;
+          for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * q4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * half) = o;
+        }
       }
     }
     if constexpr (!RET) {
@@ -536,13 +549,13 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
     order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
 }
 
-template <bool RET>
+template <bool RET, bool WO>
 hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(kThreads);
   switch (nbt) {
-    case 1: hipLaunchKernelGGL((attn_bf16_kernel<RET, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<RET, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<RET, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -569,11 +582,12 @@ hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
 }
 
 hipError_t launch_block_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
-  return launch_nbt<false>(block_tiles(a.B), batch, a, s);
+  if (a.out == nullptr) return launch_nbt<false, false>(block_tiles(a.B), batch, a, s);
+  return launch_nbt<false, true>(block_tiles(a.B), batch, a, s);
 }
 
 hipError_t launch_retained_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
-  return launch_nbt<true>(block_tiles(a.rph), batch, a, s);
+  return launch_nbt<true, true>(block_tiles(a.rph), batch, a, s);
 }
 
 }  // namespace focus

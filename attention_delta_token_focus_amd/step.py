@@ -3,7 +3,9 @@
 Order of calls per step (one stream, no host synchronisation):
   focus_schedule (longest-prefix-first visiting order, shared by the
   attention calls of the step);
-  focus_block_attn_importance on layer 0, then on layer 1;
+  focus_block_attn_importance on layer 0, then on layer 1 (with
+  l1_output=False layer 1 gets out=NULL: importance and lse only, no V
+  read, no P V product);
   focus_select (head mean, MaxPool1D, delta, top-K and the retained
   indices with per-sequence offsets, in one launch), or the same as two
   calls, focus_delta_topk then focus_compact (fused=False);
@@ -49,9 +51,11 @@ class FocusStep:
 
     def __init__(self, dims: Dims, cu_prefix_host: Sequence[int],
                  k_keep_host: Sequence[int], n_further: int = 0,
-                 device="cuda", with_lse: bool = False, fused: bool = True):
+                 device="cuda", with_lse: bool = False, fused: bool = True,
+                 l1_output: bool = True):
         self.dims = dims
         self.fused = fused
+        self.l1_output = l1_output
         dv = torch.device(device)
         n, blk, hq, d = dims.batch, dims.block, dims.hq, dims.head_dim
         cu = np.asarray(cu_prefix_host, dtype=np.int64)
@@ -62,7 +66,7 @@ class FocusStep:
         self.n_ret, self.max_ret = retained_counts(k_keep_host, blk)
         f32 = dict(device=dv, dtype=torch.float32)
         self.out = [torch.empty((n * blk, hq, d), device=dv, dtype=dims.dtype)
-                    for _ in range(2)]
+                    if w == 0 or l1_output else None for w in range(2)]
         self.imp = [torch.empty((n, hq, blk), **f32) for _ in range(2)]
         self.lse = ([torch.empty((n, hq, blk), **f32) for _ in range(2)]
                     if with_lse else [None, None])
@@ -92,8 +96,11 @@ class FocusStep:
         dm = self.dims
         focus_block_attn_importance(
             dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
-            dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
-            layer["k_cache"], layer["v_cache"], self.cu_prefix, self.order,
+            dm.head_dim, dm.scale, layer["q"], layer["k_blk"],
+            layer["v_blk"] if self.out[which] is not None else None,
+            layer["k_cache"],
+            layer["v_cache"] if self.out[which] is not None else None,
+            self.cu_prefix, self.order,
             self.max_prefix, self.out[which], self.imp[which],
             self.lse[which], self.ws, self.ws_bytes, stream)
 

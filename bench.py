@@ -41,15 +41,18 @@ ATTN_SRC = os.path.join(ROOT, "attention_delta_token_focus_amd", "csrc",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_attn_c3.json")
 
 
-def attn_bytes(cfg, prefix_lens, with_lse=False) -> int:
+def attn_bytes(cfg, prefix_lens, with_lse=False, with_out=True) -> int:
     """Algorithmic HBM bytes of one block-attention launch: Q in, O out,
-    prefix K/V and block K/V in, importance out (and lse if written)."""
+    prefix K/V and block K/V in, importance out (and lse if written).
+    Importance only (with_out=False): Q, prefix K and block K in,
+    importance out."""
     e = 2 if cfg.dtype == "bf16" else 4
     n, blk, hq, hkv, d = cfg.batch, cfg.block, cfg.hq, cfg.hkv, cfg.head_dim
-    per_seq = 2 * blk * hq * d * e + 2 * blk * hkv * d * e + 4 * hq * blk
+    f = 2 if with_out else 1
+    per_seq = f * blk * hq * d * e + f * blk * hkv * d * e + 4 * hq * blk
     if with_lse:
         per_seq += 4 * hq * blk
-    return int(n * per_seq + 2 * int(prefix_lens.sum()) * hkv * d * e)
+    return int(n * per_seq + f * int(prefix_lens.sum()) * hkv * d * e)
 
 
 def select_bytes(cfg, n_ret) -> int:
@@ -132,6 +135,46 @@ def cpu_baseline(inp, n_further, budget_s=20.0):
     }
 
 
+def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
+    """The same step with layer 1 called with out=NULL (importance and lse
+    only: no V stream, no P V), on the same tensors. Reported beside the
+    step, which produces O for both layers."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=n_further,
+                     l1_output=False)
+    layers = inp.layers
+    for _ in range(max(1, args.warmup // 2)):
+        step.run(layers)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        step.schedule()
+        step.block_attn(layers[0], 0)
+        ev[s][0].record(stream)
+        step.block_attn(layers[1], 1)
+        ev[s][1].record(stream)
+        step.select()
+        for i, lay in enumerate(layers[2:2 + n_further]):
+            step.retained(lay, i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    l1_s = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    b = attn_bytes(cfg, plen, with_out=False)
+    return {
+        "block_steps_per_s": round(cfg.batch * args.steps / (total_ms / 1e3), 1),
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "block_attn_l1_us": round(l1_s * 1e6, 2),
+        "l1_algorithmic_bytes_per_launch": b,
+        "l1_achieved_GBs": round(b / l1_s / 1e9, 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +186,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (PMC scale)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the layer-1 importance-only variant timing")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -224,6 +269,11 @@ def main() -> int:
     imp_evict_ms = (float(np.mean(sched_ms)) + float(np.mean(attn_ms)) * 2
                     + float(np.mean(sel_ms)))
 
+    variants = None
+    if not args.no_variants:
+        variants = {"layer1_importance_only": time_l1_importance_only(
+            cfg, inp, dims, n_further, args, plen)}
+
     traffic = load_traffic(cfg.name)
     result = {
         "metric": METRIC,
@@ -269,6 +319,7 @@ def main() -> int:
         "step_hbm_fraction": round(step_bytes / (ms_per_step / 1e3) / 1e9
                                    / HBM_PEAK_GBS, 4),
         "wall_s": round(wall, 3),
+        "variants": variants,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

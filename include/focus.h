@@ -115,14 +115,20 @@ focus_status focus_block_attn_importance_workspace(
  *              NULL: the call writes that order into the workspace first
  *              (one extra kernel launch).
  *  max_prefix  host promise: max_b P_b (sizes the launch).
- *  out         [batch*B, Hq, d] attention output (type dt).
+ *  out         [batch*B, Hq, d] attention output (type dt), or NULL for
+ *              importance only: then v_blk and v_cache are not read (may
+ *              be NULL) and no P V product is formed, while imp and lse
+ *              are the same values, bit for bit, as with out given. This
+ *              matches where the Pith page (Figures, Fig. 5 caption) puts
+ *              the eviction: right after layer 1's Q/K projections, so
+ *              layer 1 needs no attention output.
  *  imp         float32 [batch, Hq, B] importance of the block columns.
  *  lse         float32 [batch, Hq, B] natural-log row lse, or NULL.
  *  workspace   device scratch of at least the queried size, needed only
  *              when order is NULL; its contents on entry do not matter.
  * Errors: INVALID_ARG (null required pointer, batch < 1, B not in [1,128],
- * Hq or Hkv < 1, max_prefix < 0, misaligned pointer), UNSUPPORTED (d not
- * 64/128, bad dt, Hq % Hkv != 0), WORKSPACE, HIP.
+ * Hq or Hkv < 1, Hq > 4096, max_prefix < 0, misaligned pointer),
+ * UNSUPPORTED (d not 64/128, bad dt, Hq % Hkv != 0), WORKSPACE, HIP.
  */
 focus_status focus_block_attn_importance(
     focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,

@@ -45,7 +45,7 @@ def dims_of(cfg: workloads.FocusConfig):
 
 
 def run_gpu(inp: workloads.Inputs, layers_dev=None, n_further: Optional[int] = None,
-            with_lse: bool = True, step=None):
+            with_lse: bool = True, step=None, l1_output: bool = True):
     """Runs one block-step on the GPU; returns (step object, host results)."""
     from attention_delta_token_focus_amd.step import FocusStep
     cfg = inp.cfg
@@ -55,11 +55,12 @@ def run_gpu(inp: workloads.Inputs, layers_dev=None, n_further: Optional[int] = N
         n_further = len(layers_dev) - 2
     if step is None:
         step = FocusStep(dims_of(cfg), inp.cu_prefix, inp.meta.k_keep,
-                         n_further=n_further, with_lse=with_lse)
+                         n_further=n_further, with_lse=with_lse,
+                         l1_output=l1_output)
     step.run(layers_dev)
     torch.cuda.synchronize()
     res = dict(
-        out=[to_f32_numpy(o) for o in step.out],
+        out=[to_f32_numpy(o) if o is not None else None for o in step.out],
         imp=[i.cpu().numpy() for i in step.imp],
         lse=[l.cpu().numpy() if l is not None else None for l in step.lse],
         dI=step.dI.cpu().numpy(), keep=step.keep.cpu().numpy(),
@@ -148,8 +149,9 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
                                       sub[l]["k_cache"], sub[l]["v_cache"], sub_cu,
                                       blk, cfg.hq, cfg.hkv) for l in (0, 1)]
     for l in (0, 1):
-        assert_close(f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
-                     TOL[kind]["out"], TIGHT[kind]["out"], rel_scale=True)
+        if res["out"][l] is not None:   # None: importance-only call
+            assert_close(f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
+                         TOL[kind]["out"], TIGHT[kind]["out"], rel_scale=True)
         assert_close(f"imp L{l}", res["imp"][l][seqs], o[l][1], TOL[kind]["imp"],
                      TIGHT[kind]["imp"])
         if res["lse"][l] is not None:

@@ -66,7 +66,12 @@ def _attn(**kw):
     (dict(dt=7), F.FOCUS_ERR_UNSUPPORTED),
     (dict(q=None), F.FOCUS_ERR_INVALID_ARG),
     (dict(imp=None), F.FOCUS_ERR_INVALID_ARG),
-    (dict(out=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(out=None, k_blk=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(v_blk=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(v_cache=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(out=None, k_cache=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), F.FOCUS_ERR_INVALID_ARG),
+    (dict(Hq=8192, Hkv=8), F.FOCUS_ERR_INVALID_ARG),
     (dict(cu_prefix=None), F.FOCUS_ERR_INVALID_ARG),
     (dict(k_cache=None), F.FOCUS_ERR_INVALID_ARG),
     (dict(q=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),

@@ -187,3 +187,37 @@ def test_c3_full_size_sampled():
 
 def test_c5_full_size_sampled():
     _full_size("c5", "c5", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 64])
+
+
+@pytest.mark.parametrize("over,plens,kk", [
+    (dict(), None, None),
+    (dict(block=128, pool_k=5), [100, 0, 2100], [32, 0, 128]),
+    (dict(block=7), [5, 90, 1, 0], [0, 7, 3, 1]),
+    (dict(block=48, hq=16, hkv=2), [40, 333], [9, 48]),
+    (dict(dtype="f32", head_dim=64, hq=4, hkv=1), [70, 3], [8, 32]),
+])
+def test_layer1_importance_only(over, plens, kk):
+    """out=NULL on layer 1 (no V read, no P V): the oracle still matches
+    importance and lse, and both are bitwise those of the call with out."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 16,
+                           **over)
+    log(f"[parity] layer-1 importance only B={cfg.block} N={cfg.batch} "
+        f"{cfg.dtype} d={cfg.head_dim}")
+    inp = workloads.make_inputs(cfg, 12, n_layers=3, prefix_lens=plens, k_keep=kk)
+    lay = parity.to_device(inp)
+    step, res = parity.run_gpu(inp, layers_dev=lay, l1_output=False)
+    assert step.out[1] is None and res["out"][1] is None
+    parity.compare_step(inp, res, range(cfg.batch))
+    dm = step.dims
+    full_out = torch.empty_like(step.out[0])
+    imp = torch.empty_like(step.imp[1])
+    lse = torch.empty_like(step.lse[1])
+    L1 = lay[1]
+    F.focus_block_attn_importance(
+        F.dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv, dm.head_dim, 0.0,
+        L1["q"], L1["k_blk"], L1["v_blk"], L1["k_cache"], L1["v_cache"],
+        step.cu_prefix, step.order, step.max_prefix, full_out, imp, lse,
+        step.ws, step.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(imp, step.imp[1]) and torch.equal(lse, step.lse[1])
