@@ -25,7 +25,10 @@ same paper, cited as "ScienceStack page"):
       importance (same section, Eq. 3).
   S4  keep the K_b tokens with the largest delta (same section; Fig. 5 on
       the ScienceStack page: top candidates within the budget). Ties go to
-      the lower block position.
+      the lower block position. With a mask of the still-masked positions,
+      only those are candidates, and the retained set adds each candidate's
+      predecessor and every masked position left of the rightmost
+      candidate (the two structural constraints of the same section).
   S5  the retained tokens (ascending b*B + j, with per-sequence offsets) go
       on to the remaining layers (Pith page, "The pith"); their attention
       there sees the full prefix plus the retained block tokens only.
@@ -159,6 +162,43 @@ def topk_keep(d_imp: np.ndarray, k_keep) -> np.ndarray:
         order = sorted(range(blk), key=lambda j: (-d_imp[b, j], j))
         keep[b, order[:kb]] = 1
     return keep
+
+
+def select_constrained(d_imp: np.ndarray, masked: np.ndarray, k_keep,
+                       keep_predecessor: bool = True,
+                       keep_masked_prefix: bool = True
+                       ) -> Tuple[np.ndarray, np.ndarray]:
+    """S4 with masked-token eligibility and the two structural constraints
+    (Pith page, "What carries the argument": top-K candidates under the
+    budget, then keep each candidate's immediate predecessor and every
+    masked token before the rightmost candidate).
+
+    Per sequence b: the candidates are the min(max(K_b, 0), #masked) masked
+    positions with the largest delta, equal deltas to the lower position.
+    The retained set is the candidates, plus position j - 1 of every
+    candidate j > 0 (masked or not), plus every masked position left of the
+    rightmost candidate. No candidate: nothing is retained.
+    Returns (keep, cand), both [N, B] uint8."""
+    d_imp = np.asarray(d_imp, dtype=F64)
+    masked = np.asarray(masked).astype(bool)
+    n, blk = d_imp.shape
+    keep = np.zeros((n, blk), dtype=np.uint8)
+    cand = np.zeros((n, blk), dtype=np.uint8)
+    for b in range(n):
+        eligible = [j for j in range(blk) if masked[b, j]]
+        kb = min(max(int(k_keep[b]), 0), len(eligible))
+        chosen = sorted(eligible, key=lambda j: (-d_imp[b, j], j))[:kb]
+        for j in chosen:
+            cand[b, j] = 1
+            keep[b, j] = 1
+            if keep_predecessor and j > 0:
+                keep[b, j - 1] = 1
+        if keep_masked_prefix and chosen:
+            rightmost = max(chosen)
+            for j in range(rightmost):
+                if masked[b, j]:
+                    keep[b, j] = 1
+    return keep, cand
 
 
 def compact(keep: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

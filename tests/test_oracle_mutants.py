@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from oracle import focus_oracle
+from tests import test_oracle_constrained as PC
 from tests import test_oracle_pins as P
 
 PINS = [
@@ -32,6 +33,12 @@ PINS = [
     P.test_compact_matches_nonzero_and_cumsum,
     P.test_retained_with_full_budget_equals_block_attention,
     P.test_retained_matches_torch_sdpa_on_gathered_rows,
+    *[(lambda c=c: PC.test_golden_constrained(c)) for c in PC._cases()],
+    PC.test_golden_constrained_batched_compaction,
+    *[(lambda s=s: PC.test_constrained_matches_characterisation(s)) for s in range(6)],
+    PC.test_all_masked_without_constraints_is_plain_topk,
+    PC.test_all_masked_with_prefix_rule_keeps_a_contiguous_head,
+    PC.test_nothing_masked_retains_nothing,
 ]
 
 # (name, [(old, new, occurrence)])
@@ -74,11 +81,26 @@ MUTANTS = [
          "np.asarray(v_src[b * block:(b + 1) * block, g], F64)", 0)]),
     ("retained prefix from token 0", [("p0, p1 = int(cu_p[b]), int(cu_p[b + 1])",
                                        "p0, p1 = 0, int(cu_p[b + 1])", 0)]),
+    ("constrained: mask ignored", [(
+        "eligible = [j for j in range(blk) if masked[b, j]]",
+        "eligible = list(range(blk))", 0)]),
+    ("constrained: successor kept", [("keep[b, j - 1] = 1",
+                                      "keep[b, min(j + 1, blk - 1)] = 1", 0)]),
+    ("constrained: decoded positions in the prefix rule", [
+        ("                if masked[b, j]:", "                if True:", 0)]),
+    ("constrained: leftmost candidate", [("rightmost = max(chosen)",
+                                          "rightmost = min(chosen)", 0)]),
+    ("constrained: prefix rule to the block end", [("for j in range(rightmost):",
+                                                    "for j in range(blk):", 0)]),
+    ("constrained: ties to higher index", [("key=lambda j: (-d_imp[b, j], j)",
+                                            "key=lambda j: (-d_imp[b, j], -j)", 1)]),
+    ("constrained: smallest deltas", [("key=lambda j: (-d_imp[b, j], j)",
+                                       "key=lambda j: (d_imp[b, j], j)", 1)]),
 ]
 
 EXPORTED = ["attention_rows", "block_attn_importance", "block_step", "compact",
             "default_scale", "head_mean_maxpool", "importance_delta",
-            "retained_attn", "topk_keep"]
+            "retained_attn", "select_constrained", "topk_keep"]
 
 
 def _replace_nth(src, old, new, n):
