@@ -33,6 +33,8 @@ FOCUS_ERR_WORKSPACE = 3
 FOCUS_ERR_HIP = 4
 FOCUS_F32 = 0
 FOCUS_BF16 = 1
+FOCUS_KEEP_PREDECESSOR = 1
+FOCUS_KEEP_MASKED_PREFIX = 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "lib", "libfocus.so")
@@ -61,6 +63,8 @@ _SIGS = {
     "focus_delta_topk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "focus_compact": (_I, [_I, _I, _P, _P, _P, _P]),
     "focus_select": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "focus_select_masked": (
+        _I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]),
     "focus_retained_attn_workspace": (
         _I, [_I, _I, _I, _I, _I, _I, _I, _c.POINTER(_SZ)]),
     "focus_retained_attn": (
@@ -176,6 +180,16 @@ def focus_select(batch, B, Hq, pool_k, imp0, imp1, k_keep, keep, dI, idx,
         batch, B, Hq, pool_k, _ptr(imp0, "imp0"), _ptr(imp1, "imp1"),
         _ptr(k_keep, "k_keep"), _ptr(keep, "keep"), _ptr(dI, "dI", True),
         _ptr(idx, "idx"), _ptr(cu_ret, "cu_ret"), _stream(stream)))
+
+
+def focus_select_masked(batch, B, Hq, pool_k, imp0, imp1, masked, k_keep,
+                        rules, keep, cand=None, dI=None, idx=None, cu_ret=None,
+                        stream=None) -> None:
+    _check(lib.focus_select_masked(
+        batch, B, Hq, pool_k, _ptr(imp0, "imp0"), _ptr(imp1, "imp1"),
+        _ptr(masked, "masked", True), _ptr(k_keep, "k_keep"), int(rules),
+        _ptr(keep, "keep"), _ptr(cand, "cand", True), _ptr(dI, "dI", True),
+        _ptr(idx, "idx", True), _ptr(cu_ret, "cu_ret", True), _stream(stream)))
 
 
 def focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,

@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
   int rbase, nq;
   if constexpr (RET) {
     rbase = a.cu_ret[b];
-    nq = a.cu_ret[b + 1] - rbase;
+    nq = min(a.cu_ret[b + 1] - rbase, a.rph);  // a broken max_ret promise stays in bounds
     if (nq <= 0) return;  // uniform over the workgroup
   } else {
     rbase = b * a.B;

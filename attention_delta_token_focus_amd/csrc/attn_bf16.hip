@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   int rbase, nq;
   if constexpr (RET) {
     rbase = a.cu_ret[b];
-    nq = a.cu_ret[b + 1] - rbase;
+    nq = min(a.cu_ret[b + 1] - rbase, a.rph);  // a broken max_ret promise stays in bounds
     if (nq <= 0) return;  // uniform over the workgroup
   } else {
     rbase = b * a.B;

@@ -79,33 +79,47 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[2], int lane) {
 
 // Head mean, MaxPool1D, delta and top-K of sequence b by one wavefront
 // (lane l holds block positions l and l + 64). Writes dI and keep; returns
-// in `flag` the keep flag of positions lane and lane + 64, and kb.
+// in `flags` the keep flag of every position, and the number kept.
+//
+// With `masked` given, only positions with masked[j] != 0 are candidates
+// (at most K_b of them), and the retained set grows by the structural
+// constraints selected in `rules`: each candidate's predecessor
+// (kKeepPredecessor) and every masked position left of the rightmost
+// candidate (kKeepMaskedPrefix). `cand`, when given, receives the
+// candidate flags. Without a mask and rules this is plain top-K.
+constexpr int kKeepPredecessor = 1;
+constexpr int kKeepMaskedPrefix = 2;
+
 template <int NS>
 __device__ __forceinline__ void delta_topk_wave(
     int b, int B, int Hq, int radius, const float* __restrict__ imp0,
-    const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
-    uint8_t* __restrict__ keep, float* __restrict__ dI, float (*mean)[128],
-    uint8_t* flags, int& kb_out) {
+    const float* __restrict__ imp1, const uint8_t* __restrict__ masked,
+    int rules, const int32_t* __restrict__ k_keep, uint8_t* __restrict__ keep,
+    uint8_t* __restrict__ cand, float* __restrict__ dI, float (*mean)[128],
+    uint8_t* flags, int& n_kept) {
   const int lane = threadIdx.x;
   const float inv_h = 1.0f / (float)Hq;
   const float* i0 = imp0 + (size_t)b * Hq * B;
   const float* i1 = imp1 + (size_t)b * Hq * B;
   const int kb = min(max(k_keep[b], 0), B);
+  bool elig[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = lane + 64 * s;
+    elig[s] = j < B && (masked == nullptr || masked[(size_t)b * B + j] != 0);
     if (j < B) {
       float a0, a1;
       head_sums(i0, i1, Hq, B, j, a0, a1);
       mean[0][j] = a0 * inv_h;
       mean[1][j] = a1 * inv_h;
+      flags[j] = 0;
     }
   }
   __syncthreads();
 
   // Sort keys: (order code of dI) << 32 | (~j), so that larger dI comes
-  // first and, for equal dI, the lower position. Empty slots are 0, which
-  // is below every real key.
+  // first and, for equal dI, the lower position. Empty slots and positions
+  // that are not candidates are 0, below every real key (~j is never 0).
   uint64_t key[2] = {0, 0};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -119,33 +133,70 @@ __device__ __forceinline__ void delta_topk_wave(
       }
       const float d = m1 - m0;
       if (dI != nullptr) dI[(size_t)b * B + j] = d;
-      key[s] = ((uint64_t)order_code(d) << 32) | (uint32_t)(0xFFFFFFFFu - j);
+      if (elig[s]) key[s] = ((uint64_t)order_code(d) << 32) | (uint32_t)(0xFFFFFFFFu - j);
     }
   }
   bitonic_desc<NS>(key, lane);
+  // Candidates: the first K_b ranks that hold a real key.
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int p = lane + 64 * s;  // rank in descending order
-    if (key[s] != 0) {
-      const int j = (int)(0xFFFFFFFFu - (uint32_t)key[s]);
-      const uint8_t k = p < kb ? 1 : 0;
-      keep[(size_t)b * B + j] = k;
-      if (flags != nullptr) flags[j] = k;
+    if (key[s] != 0 && p < kb) flags[(int)(0xFFFFFFFFu - (uint32_t)key[s])] = 1;
+  }
+  __syncthreads();
+
+  // Retained set from the candidate flags, position by position.
+  int rightmost = -1;
+  if (rules & kKeepMaskedPrefix) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = lane + 64 * s;
+      if (j < B && flags[j] != 0) rightmost = max(rightmost, j);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rightmost = max(rightmost, __shfl_xor(rightmost, o));
+  }
+  uint8_t kept[NS];
+  int cnt = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = lane + 64 * s;
+    kept[s] = 0;
+    if (j < B) {
+      const bool c = flags[j] != 0;
+      bool k = c;
+      if ((rules & kKeepPredecessor) && j + 1 < B && flags[j + 1] != 0) k = true;
+      if (elig[s] && j < rightmost) k = true;
+      kept[s] = k ? 1 : 0;
+      cnt += kept[s];
+      keep[(size_t)b * B + j] = kept[s];
+      if (cand != nullptr) cand[(size_t)b * B + j] = c ? 1 : 0;
     }
   }
-  kb_out = kb;
+  __syncthreads();  // every lane has read the candidate flags
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = lane + 64 * s;
+    if (j < B) flags[j] = kept[s];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  n_kept = cnt;
+  __syncthreads();
 }
 
 // One wavefront per sequence.
 template <int NS>
 __global__ void __launch_bounds__(64) delta_topk_kernel(
     int B, int Hq, int radius, const float* __restrict__ imp0,
-    const float* __restrict__ imp1, const int32_t* __restrict__ k_keep,
-    uint8_t* __restrict__ keep, float* __restrict__ dI) {
+    const float* __restrict__ imp1, const uint8_t* __restrict__ masked,
+    int rules, const int32_t* __restrict__ k_keep, uint8_t* __restrict__ keep,
+    uint8_t* __restrict__ cand, float* __restrict__ dI) {
   __shared__ float mean[2][128];
-  int kb;
-  delta_topk_wave<NS>(blockIdx.x, B, Hq, radius, imp0, imp1, k_keep, keep, dI,
-                      mean, nullptr, kb);
+  __shared__ uint8_t flags[128];
+  int n_kept;
+  delta_topk_wave<NS>(blockIdx.x, B, Hq, radius, imp0, imp1, masked, rules, k_keep,
+                      keep, cand, dI, mean, flags, n_kept);
 }
 
 // Delta/top-K and compaction in one launch, one wavefront per sequence.
@@ -171,9 +222,8 @@ __global__ void __launch_bounds__(64) select_kernel(
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
   int kb;
-  delta_topk_wave<NS>(b, B, Hq, radius, imp0, imp1, k_keep, keep, dI, mean,
-                      flags, kb);
-  __syncthreads();
+  delta_topk_wave<NS>(b, B, Hq, radius, imp0, imp1, nullptr, 0, k_keep, keep,
+                      nullptr, dI, mean, flags, kb);
   int base = off;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -283,14 +333,17 @@ __global__ void __launch_bounds__(1024) compact_kernel(
 
 hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
-                             const int32_t* k_keep, uint8_t* keep, float* dI,
-                             hipStream_t s) {
+                             const uint8_t* masked, int rules,
+                             const int32_t* k_keep, uint8_t* keep, uint8_t* cand,
+                             float* dI, hipStream_t s) {
   if (B <= 64) {
     hipLaunchKernelGGL(delta_topk_kernel<1>, dim3(batch), dim3(64), 0, s, B, Hq,
-                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, keep,
+                       cand, dI);
   } else {
     hipLaunchKernelGGL(delta_topk_kernel<2>, dim3(batch), dim3(64), 0, s, B, Hq,
-                       (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI);
+                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, keep,
+                       cand, dI);
   }
   return hipGetLastError();
 }

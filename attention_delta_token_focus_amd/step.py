@@ -8,7 +8,10 @@ Order of calls per step (one stream, no host synchronisation):
   read, no P V product);
   focus_select (head mean, MaxPool1D, delta, top-K and the retained
   indices with per-sequence offsets, in one launch), or the same as two
-  calls, focus_delta_topk then focus_compact (fused=False);
+  calls, focus_delta_topk then focus_compact (fused=False); with a mask of
+  still-masked positions or structural rules, focus_select_masked instead
+  (the retained count is then data-dependent: the retained buffers are
+  sized for all batch*B tokens and max_ret = B);
   focus_retained_attn once per further layer.
 This module only allocates the output buffers (torch device memory) and
 calls the binding; it computes nothing itself.
@@ -24,7 +27,8 @@ import torch
 from . import (dtype_code, focus_block_attn_importance,
                focus_block_attn_importance_workspace, focus_compact,
                focus_delta_topk, focus_retained_attn,
-               focus_retained_attn_workspace, focus_schedule, focus_select)
+               focus_retained_attn_workspace, focus_schedule, focus_select,
+               focus_select_masked)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,10 +56,12 @@ class FocusStep:
     def __init__(self, dims: Dims, cu_prefix_host: Sequence[int],
                  k_keep_host: Sequence[int], n_further: int = 0,
                  device="cuda", with_lse: bool = False, fused: bool = True,
-                 l1_output: bool = True):
+                 l1_output: bool = True, masked=None, rules: int = 0):
         self.dims = dims
         self.fused = fused
         self.l1_output = l1_output
+        self.constrained = masked is not None or rules != 0
+        self.rules = rules
         dv = torch.device(device)
         n, blk, hq, d = dims.batch, dims.block, dims.hq, dims.head_dim
         cu = np.asarray(cu_prefix_host, dtype=np.int64)
@@ -64,6 +70,15 @@ class FocusStep:
         self.k_keep = torch.as_tensor(
             np.asarray(k_keep_host, dtype=np.int32), device=dv)
         self.n_ret, self.max_ret = retained_counts(k_keep_host, blk)
+        self.masked = None
+        self.cand = None
+        if self.constrained:
+            # upper bounds: every retained count is at most B
+            self.n_ret, self.max_ret = n * blk, blk
+            if masked is not None:
+                self.masked = torch.as_tensor(
+                    np.asarray(masked, dtype=np.uint8), device=dv).contiguous()
+            self.cand = torch.empty((n, blk), device=dv, dtype=torch.uint8)
         f32 = dict(device=dv, dtype=torch.float32)
         self.out = [torch.empty((n * blk, hq, d), device=dv, dtype=dims.dtype)
                     if w == 0 or l1_output else None for w in range(2)]
@@ -106,6 +121,12 @@ class FocusStep:
 
     def select(self, stream=None) -> None:
         dm = self.dims
+        if self.constrained:
+            focus_select_masked(dm.batch, dm.block, dm.hq, dm.pool_k,
+                                self.imp[0], self.imp[1], self.masked,
+                                self.k_keep, self.rules, self.keep, self.cand,
+                                self.dI, self.idx, self.cu_ret, stream)
+            return
         if self.fused:
             focus_select(dm.batch, dm.block, dm.hq, dm.pool_k, self.imp[0],
                          self.imp[1], self.k_keep, self.keep, self.dI,

@@ -197,6 +197,51 @@ focus_status focus_select(int batch, int B, int Hq, int pool_k,
                           const int32_t* k_keep, uint8_t* keep, float* dI,
                           int32_t* idx, int32_t* cu_ret, void* stream);
 
+/* Structural constraints of focus_select_masked (bit flags). */
+#define FOCUS_KEEP_PREDECESSOR 1   /* keep position j-1 of each candidate j */
+#define FOCUS_KEEP_MASKED_PREFIX 2 /* keep every masked position left of the
+                                      rightmost candidate */
+
+/*
+ * Top-K over the still-masked positions, then the two structural
+ * constraints, then (optionally) compaction.
+ *
+ * Follows the Pith page, "What carries the argument": top-K candidates by
+ * importance delta under the budget, then retain each candidate's
+ * immediate predecessor and all masked tokens before the rightmost
+ * candidate. Only tokens that are still masked can be candidates (the
+ * method predicts which masked tokens will decode; Pith page, Referee
+ * Report). Per sequence b, with M = { j : masked[b,j] != 0 } (all j if
+ * masked is NULL) and dI as in focus_delta_topk:
+ *    cand  = the min(max(k_keep[b],0), |M|) positions of M with the largest
+ *            dI, equal values ordered by lower j first;
+ *    keep  = cand
+ *            + { j-1 : j in cand, j > 0 }           if FOCUS_KEEP_PREDECESSOR
+ *            + { j in M : j < max(cand) }           if FOCUS_KEEP_MASKED_PREFIX
+ *            (nothing when cand is empty).
+ * With masked NULL and rules 0 this is focus_delta_topk (+ focus_compact).
+ * The retained count per sequence is data-dependent here: size the
+ * retained attention with n_ret = batch*B and max_ret = B (upper bounds)
+ * or read cu_ret back.
+ *
+ *  masked  uint8 [batch, B], non-zero = still masked (a candidate), or NULL.
+ *  rules   OR of FOCUS_KEEP_PREDECESSOR and FOCUS_KEEP_MASKED_PREFIX.
+ *  keep    uint8 [batch, B] output: the retained set.
+ *  cand    uint8 [batch, B] output: the top-K candidates, or NULL.
+ *  dI      float32 [batch, B] output, or NULL.
+ *  idx, cu_ret  as focus_compact over keep, or both NULL (no compaction).
+ * Two kernels: the selection (one wavefront per sequence) and, when idx is
+ * given, the one-workgroup compaction.
+ * Errors: as focus_delta_topk; INVALID_ARG if exactly one of idx / cu_ret
+ * is NULL; UNSUPPORTED for unknown rule bits.
+ */
+focus_status focus_select_masked(int batch, int B, int Hq, int pool_k,
+                                 const float* imp0, const float* imp1,
+                                 const uint8_t* masked, const int32_t* k_keep,
+                                 int rules, uint8_t* keep, uint8_t* cand,
+                                 float* dI, int32_t* idx, int32_t* cu_ret,
+                                 void* stream);
+
 /* Workspace bytes that focus_retained_attn needs for these sizes. */
 focus_status focus_retained_attn_workspace(
     int batch, int Hq, int Hkv, int d, int max_prefix, int n_ret,
@@ -211,8 +256,12 @@ focus_status focus_retained_attn_workspace(
  *  q_src       [batch*B, Hq, d]  the layer's block queries; rows read via idx.
  *  k_src,v_src [batch*B, Hkv, d] the layer's block keys/values; via idx.
  *  idx, cu_ret from focus_compact (device).
- *  n_ret       host promise: cu_ret[batch] (rows of out).
- *  max_ret     host promise: max_b (cu_ret[b+1] - cu_ret[b]), <= B.
+ *  n_ret       host promise: cu_ret[batch] <= n_ret (rows of out); an
+ *              upper bound such as batch*B is allowed (rows past
+ *              cu_ret[batch] are left untouched).
+ *  max_ret     host promise: max_b (cu_ret[b+1] - cu_ret[b]) <= max_ret
+ *              <= B. Sizes the launch; a sequence with more retained rows
+ *              than max_ret only gets its first max_ret rows computed.
  *  k_cache,v_cache,cu_prefix,order,max_prefix  as in
  *              focus_block_attn_importance, for this layer.
  *  out         [n_ret, Hq, d] (type dt), row r is the query of idx[r].

@@ -64,6 +64,7 @@ def run_gpu(inp: workloads.Inputs, layers_dev=None, n_further: Optional[int] = N
         imp=[i.cpu().numpy() for i in step.imp],
         lse=[l.cpu().numpy() if l is not None else None for l in step.lse],
         dI=step.dI.cpu().numpy(), keep=step.keep.cpu().numpy(),
+        cand=step.cand.cpu().numpy() if step.cand is not None else None,
         idx=step.idx.cpu().numpy()[:step.n_ret],
         cu_ret=step.cu_ret.cpu().numpy(),
         ret=[to_f32_numpy(r)[:step.n_ret] for r in step.ret_out])
@@ -209,3 +210,64 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
             assert_close(f"retained L{2 + li}", got, want, TOL[kind]["out"],
                          TIGHT[kind]["out"], rel_scale=True)
     return rep
+
+
+def compare_constrained(inp: workloads.Inputs, res, masked, rules: int):
+    """The masked-candidate selection with structural rules against the
+    oracle's own selection on the oracle's own importance (all sequences),
+    plus the retained attention of the further layers on exactly matched
+    sequences. The GPU's result must also be a valid selection of its own
+    delta (set-based characterisation)."""
+    from tests.test_oracle_constrained import _characterise
+    cfg = inp.cfg
+    blk, kind, n = cfg.block, cfg.dtype, cfg.batch
+    pred, mpre = bool(rules & 1), bool(rules & 2)
+    seqs = list(range(n))
+    sub, sub_cu = sub_layers(inp.layers, inp.cu_prefix, blk, seqs)
+    o = [oracle.block_attn_importance(sub[l]["q"], sub[l]["k_blk"], sub[l]["v_blk"],
+                                      sub[l]["k_cache"], sub[l]["v_cache"], sub_cu,
+                                      blk, cfg.hq, cfg.hkv) for l in (0, 1)]
+    for l in (0, 1):
+        assert_close(f"imp L{l}", res["imp"][l], o[l][1], TOL[kind]["imp"],
+                     TIGHT[kind]["imp"])
+    dI_ref = oracle.importance_delta(o[0][1], o[1][1], cfg.pool_k)
+    assert_close("dI", res["dI"], dI_ref, TIGHT[kind]["dI"])
+    k_keep = inp.meta.k_keep
+    keep_ref, cand_ref = oracle.select_constrained(dI_ref, masked, k_keep, pred, mpre)
+    exact, excused = [], 0
+    for b in seqs:
+        _characterise(res["dI"][b].astype(np.float64), masked[b], int(k_keep[b]),
+                      pred, mpre, res["keep"][b], res["cand"][b])
+        if (np.array_equal(res["keep"][b], keep_ref[b])
+                and np.array_equal(res["cand"][b], cand_ref[b])):
+            exact.append(b)
+            continue
+        elig = [j for j in range(blk) if masked[b, j]]
+        order = sorted(elig, key=lambda j: (-dI_ref[b, j], j))
+        kb = min(max(int(k_keep[b]), 0), len(elig))
+        assert 0 < kb < len(elig), f"seq {b}: mismatch without a tie candidate"
+        gap = dI_ref[b, order[kb - 1]] - dI_ref[b, order[kb]]
+        assert gap < GAP, f"seq {b}: gpu {np.flatnonzero(res['cand'][b])} " \
+                          f"oracle {np.flatnonzero(cand_ref[b])} gap {gap}"
+        excused += 1
+    log(f"  constrained selection: {len(exact)} exact, {excused} excused")
+    # compaction of the GPU's own retained set
+    cnt = res["keep"].sum(axis=1)
+    cu = res["cu_ret"]
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), cnt)
+    total = int(cu[-1])
+    assert np.array_equal(res["idx"][:total], np.flatnonzero(res["keep"].ravel()))
+    # retained attention of the further layers on exactly matched sequences
+    idx_ref, cu_ref = oracle.compact(keep_ref)
+    for li, ret in enumerate(res["ret"]):
+        lay = sub[2 + li]
+        ref = oracle.retained_attn(lay["q"], lay["k_blk"], lay["v_blk"], idx_ref,
+                                   cu_ref, lay["k_cache"], lay["v_cache"], sub_cu,
+                                   blk, cfg.hq, cfg.hkv)
+        got = [ret[cu[b]:cu[b + 1]] for b in exact if cu[b + 1] > cu[b]]
+        want = [ref[cu_ref[b]:cu_ref[b + 1]] for b in exact if cu[b + 1] > cu[b]]
+        if got:
+            assert_close(f"retained L{2 + li}", np.concatenate(got),
+                         np.concatenate(want), TOL[kind]["out"], TIGHT[kind]["out"],
+                         rel_scale=True)
+    return exact

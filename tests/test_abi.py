@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(F.lib, name), name
         assert callable(getattr(F, name)), name
@@ -134,6 +134,30 @@ def test_select_rejects_bad_arguments(kw, code):
     assert F.lib.focus_select(a["batch"], a["B"], a["Hq"], a["pool_k"],
                               a["imp0"], a["imp1"], a["k_keep"], a["keep"],
                               a["dI"], a["idx"], a["cu_ret"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(B=129), F.FOCUS_ERR_INVALID_ARG),
+    (dict(pool_k=2), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(rules=4), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(rules=-1), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(keep=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(k_keep=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(idx=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(cu_ret=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(imp1=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),
+])
+def test_select_masked_rejects_bad_arguments(kw, code):
+    a = dict(batch=2, B=32, Hq=32, pool_k=3, imp0=FAKE, imp1=FAKE, masked=FAKE,
+             k_keep=FAKE, rules=3, keep=FAKE, cand=None, dI=None, idx=FAKE,
+             cu_ret=FAKE)
+    a.update(kw)
+    assert F.lib.focus_select_masked(
+        a["batch"], a["B"], a["Hq"], a["pool_k"], a["imp0"], a["imp1"],
+        a["masked"], a["k_keep"], a["rules"], a["keep"], a["cand"], a["dI"],
+        a["idx"], a["cu_ret"], None) == code
+    assert F.focus_last_error().startswith("focus_select_masked")
 
 
 def _ret(**kw):

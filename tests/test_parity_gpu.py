@@ -221,3 +221,53 @@ def test_layer1_importance_only(over, plens, kk):
         step.ws, step.ws_bytes)
     torch.cuda.synchronize()
     assert torch.equal(imp, step.imp[1]) and torch.equal(lse, step.lse[1])
+
+
+MASKED = [
+    # overrides, prefix lengths, budgets, rules
+    (dict(), None, None, 3),
+    (dict(), None, None, 1),
+    (dict(), None, None, 2),
+    (dict(), None, None, 0),
+    (dict(block=128, pool_k=5), [100, 0, 2100], [32, 0, 128], 3),
+    (dict(block=7), [5, 90, 1, 0], [0, 7, 3, 1], 3),
+    (dict(block=64, hq=8, hkv=2), [64, 1, 200], [1, 64, 20], 3),
+]
+
+
+@pytest.mark.parametrize("over,plens,kk,rules", MASKED,
+                         ids=[f"B{m[0].get('block', 32)}-rules{m[3]}-{i}"
+                              for i, m in enumerate(MASKED)])
+def test_masked_candidates_and_structural_constraints(over, plens, kk, rules):
+    from attention_delta_token_focus_amd.step import FocusStep
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 24,
+                           **over)
+    log(f"[parity] masked selection rules={rules} B={cfg.block} N={cfg.batch}")
+    inp = workloads.make_inputs(cfg, 21, n_layers=3, prefix_lens=plens, k_keep=kk)
+    masked = workloads.draw_masked(cfg, 21)
+    step = FocusStep(parity.dims_of(cfg), inp.cu_prefix, inp.meta.k_keep,
+                     n_further=1, with_lse=True, masked=masked, rules=rules)
+    step, res = parity.run_gpu(inp, step=step)
+    parity.compare_constrained(inp, res, masked, rules)
+
+
+def test_masked_select_without_mask_or_rules_equals_focus_select():
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=40)
+    log("[parity] focus_select_masked(NULL, 0) == focus_select")
+    inp = workloads.make_inputs(cfg, 22, n_layers=2)
+    step, r1 = parity.run_gpu(inp)
+    dm = step.dims
+    keep = torch.zeros_like(step.keep)
+    cand = torch.zeros_like(step.keep)
+    dI = torch.zeros_like(step.dI)
+    idx = torch.full_like(step.idx, -3)
+    cu = torch.zeros_like(step.cu_ret)
+    F.focus_select_masked(dm.batch, dm.block, dm.hq, dm.pool_k, step.imp[0],
+                          step.imp[1], None, step.k_keep, 0, keep, cand, dI, idx, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(keep.cpu(), torch.from_numpy(r1["keep"]))
+    assert torch.equal(cand, keep)
+    assert torch.equal(dI.cpu(), torch.from_numpy(r1["dI"]))
+    assert torch.equal(cu.cpu(), torch.from_numpy(r1["cu_ret"]))
+    assert np.array_equal(idx.cpu().numpy()[:step.n_ret], r1["idx"])

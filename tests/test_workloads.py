@@ -74,3 +74,15 @@ def test_planted_bias_moves_planted_keys_along_mean_query_direction():
                                            atol=1e-6, rtol=1e-5)
             else:
                 assert (diff[b, j] == 0).all()
+
+
+def test_masked_flags_are_seeded_and_left_biased():
+    cfg = workloads.get("c3")
+    a = workloads.draw_masked(cfg, 0)
+    b = workloads.draw_masked(cfg, 0)
+    c = workloads.draw_masked(cfg, 1)
+    assert a.shape == (cfg.batch, cfg.block) and a.dtype == np.uint8
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert set(np.unique(a).tolist()) <= {0, 1}
+    # earlier positions are decoded (0) more often than later ones
+    assert a[:, :8].mean() < a[:, -8:].mean()

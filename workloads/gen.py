@@ -13,6 +13,9 @@ Recipe (per configuration, per seed):
   * per layer, Q / block K,V / prefix K,V are i.i.d. N(0, 1) float32 rounded
     to bf16 by round-to-nearest-even (float32 configs keep the float32
     values);
+  * still-masked flags (for the masked-candidate selection): decoded
+    fraction f_b ~ U[0, 0.75], position j decoded with probability
+    clip(f_b * (1.5 - j / B), 0, 1);
   * layer 1 only: the block keys of planted tokens get + bias * u_hat, where
     u is the mean of that sequence's layer-1 block queries over the B
     positions and the G query heads of the key's KV group, u_hat = u / |u|,
@@ -83,6 +86,23 @@ def draw_metadata(cfg: FocusConfig, seed: int = 0) -> Metadata:
         cnt = max(1, int(np.rint(pfrac[b] * blk)))
         planted[b, rng.choice(blk, size=min(cnt, blk), replace=False)] = True
     return Metadata(plen, k_keep, planted)
+
+
+def draw_masked(cfg: FocusConfig, seed: int = 0,
+                decoded_max: float = 0.75) -> np.ndarray:
+    """Still-masked flags [N, B] uint8 for a later denoising step of the
+    block: sequence b has decoded fraction f_b ~ U[0, decoded_max], and
+    position j is already decoded with probability
+    clip(f_b * (1.5 - j / B), 0, 1) (earlier positions decode first, as in
+    semi-autoregressive block decoding). 1 = still masked."""
+    rng = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([_ROOT, cfg.index, seed, 0x4D41534B])))
+    n, blk = cfg.batch, cfg.block
+    f = rng.uniform(0.0, decoded_max, n)
+    pos = np.arange(blk) / blk
+    p_dec = np.clip(f[:, None] * (1.5 - pos[None, :]), 0.0, 1.0)
+    decoded = rng.random((n, blk)) < p_dec
+    return (~decoded).astype(np.uint8)
 
 
 def _randn(shape, cfg, seed, layer, name, device) -> torch.Tensor:
