@@ -60,6 +60,9 @@ _SIGS = {
     "focus_block_attn_importance": (
         _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _P,
              _I, _P, _P, _P, _P, _SZ, _P]),
+    "focus_block_attn_importance_paged": (
+        _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _I,
+             _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "focus_delta_topk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "focus_compact": (_I, [_I, _I, _P, _P, _P, _P]),
     "focus_select": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -70,6 +73,9 @@ _SIGS = {
     "focus_retained_attn": (
         _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _I, _I,
              _P, _P, _P, _P, _I, _P, _P, _SZ, _P]),
+    "focus_retained_attn_paged": (
+        _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _I, _I,
+             _P, _P, _P, _I, _I, _P, _P, _I, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -161,6 +167,24 @@ def focus_block_attn_importance(dt, batch, B, Hq, Hkv, d, scale, q, k_blk,
         _stream(stream)))
 
 
+def focus_block_attn_importance_paged(dt, batch, B, Hq, Hkv, d, scale, q,
+                                      k_blk, v_blk, k_pages, v_pages,
+                                      page_table, page_size, pages_per_seq,
+                                      cu_prefix, order, max_prefix, out, imp,
+                                      lse=None, workspace=None,
+                                      workspace_bytes=0, stream=None) -> None:
+    _check(lib.focus_block_attn_importance_paged(
+        dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
+        _ptr(q, "q"), _ptr(k_blk, "k_blk"), _ptr(v_blk, "v_blk", True),
+        _ptr(k_pages, "k_pages", True), _ptr(v_pages, "v_pages", True),
+        _ptr(page_table, "page_table", True), page_size, pages_per_seq,
+        _ptr(cu_prefix, "cu_prefix"), _ptr(order, "order", True),
+        max_prefix, _ptr(out, "out", True),
+        _ptr(imp, "imp"), _ptr(lse, "lse", True),
+        _ptr(workspace, "workspace", True), workspace_bytes,
+        _stream(stream)))
+
+
 def focus_delta_topk(batch, B, Hq, pool_k, imp0, imp1, k_keep, keep,
                      dI=None, stream=None) -> None:
     _check(lib.focus_delta_topk(
@@ -210,6 +234,24 @@ def focus_retained_attn(dt, batch, B, Hq, Hkv, d, scale, q_src, k_src,
         _ptr(idx, "idx", n_ret == 0), _ptr(cu_ret, "cu_ret", n_ret == 0),
         n_ret, max_ret, _ptr(k_cache, "k_cache", True),
         _ptr(v_cache, "v_cache", True), _ptr(cu_prefix, "cu_prefix"),
+        _ptr(order, "order", True), max_prefix, _ptr(out, "out", n_ret == 0),
+        _ptr(workspace, "workspace", True), workspace_bytes,
+        _stream(stream)))
+
+
+def focus_retained_attn_paged(dt, batch, B, Hq, Hkv, d, scale, q_src, k_src,
+                              v_src, idx, cu_ret, n_ret, max_ret, k_pages,
+                              v_pages, page_table, page_size, pages_per_seq,
+                              cu_prefix, order, max_prefix, out,
+                              workspace=None, workspace_bytes=0,
+                              stream=None) -> None:
+    _check(lib.focus_retained_attn_paged(
+        dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
+        _ptr(q_src, "q_src"), _ptr(k_src, "k_src"), _ptr(v_src, "v_src"),
+        _ptr(idx, "idx", n_ret == 0), _ptr(cu_ret, "cu_ret", n_ret == 0),
+        n_ret, max_ret, _ptr(k_pages, "k_pages", True),
+        _ptr(v_pages, "v_pages", True), _ptr(page_table, "page_table", True),
+        page_size, pages_per_seq, _ptr(cu_prefix, "cu_prefix"),
         _ptr(order, "order", True), max_prefix, _ptr(out, "out", n_ret == 0),
         _ptr(workspace, "workspace", True), workspace_bytes,
         _stream(stream)))

@@ -105,6 +105,171 @@ float log2_scale(float scale, int d) {
   return s * 1.4426950408889634f;
 }
 
+// Page-table arguments of the paged entry points (none for the packed
+// layout).
+struct Paging {
+  const int32_t* table = nullptr;
+  int page_size = 0;
+  int pages_per_seq = 0;
+};
+
+focus_status check_paging(const char* fn, const Paging& pg, int max_prefix) {
+  if (pg.page_size < 32 || pg.page_size % 32 != 0)
+    return fail(FOCUS_ERR_UNSUPPORTED, "%s: page_size %d is not a positive multiple of 32",
+                fn, pg.page_size);
+  if (pg.pages_per_seq < 0 ||
+      (int64_t)pg.pages_per_seq * pg.page_size < (int64_t)max_prefix)
+    return fail(FOCUS_ERR_INVALID_ARG,
+                "%s: pages_per_seq %d x page_size %d < max_prefix %d", fn,
+                pg.pages_per_seq, pg.page_size, max_prefix);
+  if (max_prefix > 0 && pg.table == nullptr)
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: page_table is NULL", fn);
+  if (pg.table != nullptr && !aligned16(pg.table))
+    return fail(FOCUS_ERR_INVALID_ARG, "%s: page_table is not 16-byte aligned", fn);
+  return FOCUS_OK;
+}
+
+focus_status block_attn_impl(
+    const char* fn, focus_dtype dt, int batch, int B, int Hq, int Hkv, int d,
+    float scale, const void* q, const void* k_blk, const void* v_blk,
+    const void* k_cache, const void* v_cache, const Paging* pg,
+    const int32_t* cu_prefix, const int32_t* order, int max_prefix, void* out,
+    float* imp, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
+    if (st != FOCUS_OK) return st;
+    if (pg != nullptr) {
+      st = check_paging(fn, *pg, max_prefix);
+      if (st != FOCUS_OK) return st;
+    }
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k_blk);
+    REQUIRE_PTR(cu_prefix);
+    REQUIRE_PTR(imp);
+    OPTIONAL_PTR(out);
+    OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(order);
+    OPTIONAL_PTR(workspace);
+    // out == NULL: importance (and lse) only; the values are not read.
+    if (out != nullptr) REQUIRE_PTR(v_blk);
+    if (max_prefix > 0) {
+      REQUIRE_PTR(k_cache);
+      if (out != nullptr) REQUIRE_PTR(v_cache);
+    }
+    size_t need = 0;
+    st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);
+    if (st != FOCUS_OK) return st;
+    if (order != nullptr) need = 0;  // the workspace only holds our own order
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
+                  fn, workspace_bytes, need);
+    focus::AttnArgs a = {};
+    a.q = q;
+    a.k_blk = k_blk;
+    a.v_blk = v_blk;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cu_prefix = cu_prefix;
+    a.out = out;
+    a.imp = imp;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.rph = B;
+    head_chunks(a.G, B, &a.hpw, &a.n_hc);
+    a.sl2 = log2_scale(scale, d);
+    if (pg != nullptr) {
+      a.page_table = pg->table;
+      a.page_size = pg->page_size;
+      a.pages_per_seq = pg->pages_per_seq;
+    }
+    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
+    return hip_status(focus::launch_block_attn(e, d, batch, a, (hipStream_t)stream),
+                      "block attention launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status retained_attn_impl(
+    const char* fn, focus_dtype dt, int batch, int B, int Hq, int Hkv, int d,
+    float scale, const void* q_src, const void* k_src, const void* v_src,
+    const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
+    const void* k_cache, const void* v_cache, const Paging* pg,
+    const int32_t* cu_prefix, const int32_t* order, int max_prefix, void* out,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
+    if (st != FOCUS_OK) return st;
+    if (pg != nullptr) {
+      st = check_paging(fn, *pg, max_prefix);
+      if (st != FOCUS_OK) return st;
+    }
+    if (n_ret < 0) return fail(FOCUS_ERR_INVALID_ARG, "%s: n_ret %d < 0", fn, n_ret);
+    if (max_ret < 0 || max_ret > B)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret %d outside [0, B=%d]", fn,
+                  max_ret, B);
+    if (n_ret > 0 && max_ret == 0)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret is 0 but n_ret is %d", fn, n_ret);
+    if (n_ret == 0) return ok();
+    REQUIRE_PTR(q_src);
+    REQUIRE_PTR(k_src);
+    REQUIRE_PTR(v_src);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(cu_ret);
+    REQUIRE_PTR(cu_prefix);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(order);
+    OPTIONAL_PTR(workspace);
+    if (max_prefix > 0) {
+      REQUIRE_PTR(k_cache);
+      REQUIRE_PTR(v_cache);
+    }
+    size_t need = 0;
+    st = focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
+                                       max_ret, &need);
+    if (st != FOCUS_OK) return st;
+    if (order != nullptr) need = 0;  // the workspace only holds our own order
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
+                  fn, workspace_bytes, need);
+    focus::AttnArgs a = {};
+    a.q = q_src;
+    a.k_blk = k_src;
+    a.v_blk = v_src;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cu_prefix = cu_prefix;
+    a.idx = idx;
+    a.cu_ret = cu_ret;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.rph = max_ret;
+    head_chunks(a.G, max_ret, &a.hpw, &a.n_hc);
+    a.sl2 = log2_scale(scale, d);
+    if (pg != nullptr) {
+      a.page_table = pg->table;
+      a.page_size = pg->page_size;
+      a.pages_per_seq = pg->pages_per_seq;
+    }
+    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
+    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "work-order launch");
+    return hip_status(
+        focus::launch_retained_attn(e, d, batch, a, (hipStream_t)stream),
+        "retained attention launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,56 +321,27 @@ focus_status focus_block_attn_importance(
     const void* v_cache, const int32_t* cu_prefix, const int32_t* order,
     int max_prefix, void* out, float* imp, float* lse, void* workspace,
     size_t workspace_bytes, void* stream) {
-  const char* fn = "focus_block_attn_importance";
-  try {
-    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
-    if (st != FOCUS_OK) return st;
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(k_blk);
-    REQUIRE_PTR(cu_prefix);
-    REQUIRE_PTR(imp);
-    OPTIONAL_PTR(out);
-    OPTIONAL_PTR(lse);
-    OPTIONAL_PTR(order);
-    OPTIONAL_PTR(workspace);
-    // out == NULL: importance (and lse) only; the values are not read.
-    if (out != nullptr) REQUIRE_PTR(v_blk);
-    if (max_prefix > 0) {
-      REQUIRE_PTR(k_cache);
-      if (out != nullptr) REQUIRE_PTR(v_cache);
-    }
-    size_t need = 0;
-    st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);
-    if (st != FOCUS_OK) return st;
-    if (order != nullptr) need = 0;  // the workspace only holds our own order
-    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
-      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
-                  fn, workspace_bytes, need);
-    focus::AttnArgs a = {};
-    a.q = q;
-    a.k_blk = k_blk;
-    a.v_blk = v_blk;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.cu_prefix = cu_prefix;
-    a.out = out;
-    a.imp = imp;
-    a.lse = lse;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = Hq / Hkv;
-    a.rph = B;
-    head_chunks(a.G, B, &a.hpw, &a.n_hc);
-    a.sl2 = log2_scale(scale, d);
-    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
-    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
-    if (he != hipSuccess) return hip_status(he, "work-order launch");
-    return hip_status(focus::launch_block_attn(e, d, batch, a, (hipStream_t)stream),
-                      "block attention launch");
-  } catch (...) {
-    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
-  }
+  return block_attn_impl("focus_block_attn_importance", dt, batch, B, Hq, Hkv, d,
+                         scale, q, k_blk, v_blk, k_cache, v_cache, nullptr,
+                         cu_prefix, order, max_prefix, out, imp, lse, workspace,
+                         workspace_bytes, stream);
+}
+
+focus_status focus_block_attn_importance_paged(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk, const void* k_pages,
+    const void* v_pages, const int32_t* page_table, int page_size,
+    int pages_per_seq, const int32_t* cu_prefix, const int32_t* order,
+    int max_prefix, void* out, float* imp, float* lse, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  Paging pg;
+  pg.table = page_table;
+  pg.page_size = page_size;
+  pg.pages_per_seq = pages_per_seq;
+  return block_attn_impl("focus_block_attn_importance_paged", dt, batch, B, Hq, Hkv,
+                         d, scale, q, k_blk, v_blk, k_pages, v_pages, &pg, cu_prefix,
+                         order, max_prefix, out, imp, lse, workspace, workspace_bytes,
+                         stream);
 }
 
 focus_status focus_delta_topk(int batch, int B, int Hq, int pool_k,
@@ -329,64 +465,28 @@ focus_status focus_retained_attn(
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
     const int32_t* order, int max_prefix, void* out, void* workspace,
     size_t workspace_bytes, void* stream) {
-  const char* fn = "focus_retained_attn";
-  try {
-    focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
-    if (st != FOCUS_OK) return st;
-    if (n_ret < 0) return fail(FOCUS_ERR_INVALID_ARG, "%s: n_ret %d < 0", fn, n_ret);
-    if (max_ret < 0 || max_ret > B)
-      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret %d outside [0, B=%d]", fn,
-                  max_ret, B);
-    if (n_ret > 0 && max_ret == 0)
-      return fail(FOCUS_ERR_INVALID_ARG, "%s: max_ret is 0 but n_ret is %d", fn, n_ret);
-    if (n_ret == 0) return ok();
-    REQUIRE_PTR(q_src);
-    REQUIRE_PTR(k_src);
-    REQUIRE_PTR(v_src);
-    REQUIRE_PTR(idx);
-    REQUIRE_PTR(cu_ret);
-    REQUIRE_PTR(cu_prefix);
-    REQUIRE_PTR(out);
-    OPTIONAL_PTR(order);
-    OPTIONAL_PTR(workspace);
-    if (max_prefix > 0) {
-      REQUIRE_PTR(k_cache);
-      REQUIRE_PTR(v_cache);
-    }
-    size_t need = 0;
-    st = focus_retained_attn_workspace(batch, Hq, Hkv, d, max_prefix, n_ret,
-                                       max_ret, &need);
-    if (st != FOCUS_OK) return st;
-    if (order != nullptr) need = 0;  // the workspace only holds our own order
-    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
-      return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
-                  fn, workspace_bytes, need);
-    focus::AttnArgs a = {};
-    a.q = q_src;
-    a.k_blk = k_src;
-    a.v_blk = v_src;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.cu_prefix = cu_prefix;
-    a.idx = idx;
-    a.cu_ret = cu_ret;
-    a.out = out;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = Hq / Hkv;
-    a.rph = max_ret;
-    head_chunks(a.G, max_ret, &a.hpw, &a.n_hc);
-    a.sl2 = log2_scale(scale, d);
-    const focus::Elem e = dt == FOCUS_BF16 ? focus::Elem::BF16 : focus::Elem::F32;
-    hipError_t he = plan_order(batch, cu_prefix, order, workspace, &a, (hipStream_t)stream);
-    if (he != hipSuccess) return hip_status(he, "work-order launch");
-    return hip_status(
-        focus::launch_retained_attn(e, d, batch, a, (hipStream_t)stream),
-        "retained attention launch");
-  } catch (...) {
-    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
-  }
+  return retained_attn_impl("focus_retained_attn", dt, batch, B, Hq, Hkv, d, scale,
+                            q_src, k_src, v_src, idx, cu_ret, n_ret, max_ret, k_cache,
+                            v_cache, nullptr, cu_prefix, order, max_prefix, out,
+                            workspace, workspace_bytes, stream);
+}
+
+focus_status focus_retained_attn_paged(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q_src, const void* k_src, const void* v_src,
+    const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
+    const void* k_pages, const void* v_pages, const int32_t* page_table,
+    int page_size, int pages_per_seq, const int32_t* cu_prefix,
+    const int32_t* order, int max_prefix, void* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  Paging pg;
+  pg.table = page_table;
+  pg.page_size = page_size;
+  pg.pages_per_seq = pages_per_seq;
+  return retained_attn_impl("focus_retained_attn_paged", dt, batch, B, Hq, Hkv, d,
+                            scale, q_src, k_src, v_src, idx, cu_ret, n_ret, max_ret,
+                            k_pages, v_pages, &pg, cu_prefix, order, max_prefix, out,
+                            workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

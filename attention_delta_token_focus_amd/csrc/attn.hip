@@ -181,7 +181,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
                    : min(kTile, nq - (t - npt) * kTile);
   };
   auto tile_row = [&](int t, int key) -> size_t {
-    if (t < npt) return (size_t)(p0 + t * kTile + key);
+    if (t < npt) {
+      const int tok = t * kTile + key;
+      if (a.page_table == nullptr) return (size_t)(p0 + tok);
+      const int32_t* ptab = a.page_table + (size_t)b * a.pages_per_seq;
+      return (size_t)ptab[tok / a.page_size] * a.page_size + tok % a.page_size;
+    }
     const int j = (t - npt) * kTile + key;
     if constexpr (RET) return (size_t)a.idx[rbase + j];
     return (size_t)(rbase + j);

@@ -43,6 +43,10 @@ template <bool WO> constexpr int stage_bytes() { return WO ? 2 * TILEB : TILEB; 
 static_assert(kRowsPerWG * PPITCH * 4 <= NSTAGE * TILEB, "pass-2 buffer fits the ring");
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before O is rescaled
+constexpr int kPageRegs = 4;    // paged prefix: registers of cached page entries
+// s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -134,7 +138,8 @@ __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
 // WO: O is produced. Without it (importance only: block mode with out =
 // NULL) no V is loaded and no P V product is formed; the K-only ring is half
 // the size and three workgroups share a CU.
-template <bool RET, int NBT, bool WO>
+// PAGED: the prefix K/V live in pages (AttnArgs::page_table).
+template <bool RET, int NBT, bool WO, bool PAGED>
 __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const AttnArgs a) {
   constexpr int STAGEB = stage_bytes<WO>();
   constexpr int SMEM = NSTAGE * STAGEB;
@@ -216,48 +221,106 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
     voff[i] = rb + ((pchunk ^ ((lr & 3) << 2)) << 4);
   }
 
+  // Paged prefix (PAGED): a cursor over the sequence's pages follows the
+  // tiles, which are issued strictly in order; pages hold a multiple of 32
+  // tokens, so a tile never straddles two pages. The page entries are held
+  // in registers, lane l of register k holding entry pg_base + 64k + l, and
+  // read with v_readlane: a scalar load of the page table in the loop would
+  // make every later LDS wait a full lgkmcnt(0), stalling on that load.
+  // Past 64 * kPageRegs pages the cache is refilled once the ring has
+  // drained (one drain per 64 * kPageRegs pages).
+  [[maybe_unused]] const int32_t* ptab = nullptr;
+  [[maybe_unused]] int pg_tiles = 1, pg_count = 0, pg_i = 0, pg_t = 0, pg_base = 0;
+  [[maybe_unused]] int pg_cache[kPageRegs];
+  auto load_page_cache = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < kPageRegs; ++k) {
+      const int i = base + 64 * k + lane;
+      pg_cache[k] = i < pg_count ? ptab[i] : 0;
+    }
+  };
+  if constexpr (PAGED) {
+    ptab = a.page_table + (size_t)b * a.pages_per_seq;
+    pg_tiles = a.page_size / TK;
+    pg_count = (plen + a.page_size - 1) / a.page_size;
+    load_page_cache(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+  // Row of the first token of prefix tile t (called once per prefix tile,
+  // t = 0, 1, 2, ... in order).
+  auto prefix_row0 = [&](int t) -> int64_t {
+    if constexpr (!PAGED) {
+      return (int64_t)p0 + t * TK;
+    } else {
+      int rel = pg_i - pg_base;
+      if (rel >= 64 * kPageRegs) {
+        // drain the ring, refill, and wait with the builtin so that the
+        // compiler sees the refill complete (no wait of its own later)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        pg_base = pg_i;
+        load_page_cache(pg_base);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        rel = 0;
+      }
+      int entry = 0;
+#pragma unroll
+      for (int k = 0; k < kPageRegs; ++k)
+        if ((rel >> 6) == k) entry = __builtin_amdgcn_readlane(pg_cache[k], rel & 63);
+      const int64_t r = (int64_t)entry * a.page_size + (int64_t)pg_t * TK;
+      if (++pg_t == pg_tiles) {
+        pg_t = 0;
+        ++pg_i;
+      }
+      return r;
+    }
+  };
+
   // Tiles 0 .. npt-1 are the prefix, npt .. nt-1 the block.
   auto issue_tile = [&](int t) {
     char* st = smem + (t % NSTAGE) * STAGEB;
-    if ((t + 1) * TK <= plen) {
-      // full prefix tile
-      const size_t tb = (size_t)(p0 + t * TK) * rowstride;
+    if (t < npt) {
+      const int64_t r0 = prefix_row0(t);
+      if ((t + 1) * TK <= plen) {
+        // full prefix tile
+        const size_t tb = (size_t)r0 * rowstride;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          char* dst = st + (2 * wave + i) * 1024;
+          dma16(kc + tb + koff[i], dst);
+          if constexpr (WO) dma16(vc + tb + voff[i], dst + TILEB);
+        }
+        return;
+      }
+      // last, partial prefix tile: rows past the end repeat the last row
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
+        const int lr = lrow0 + 4 * i;          // row inside the tile
+        const int64_t row = r0 + min(lr, plen - 1 - t * TK);
+        // koff/voff hold lr * rowstride; take it back out in integers
+        const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
         char* dst = st + (2 * wave + i) * 1024;
-        dma16(kc + tb + koff[i], dst);
-        if constexpr (WO) dma16(vc + tb + voff[i], dst + TILEB);
+        dma16(kc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
+        if constexpr (WO) dma16(vc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
       }
       return;
     }
+    const int bt = t - npt;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int lr = lrow0 + 4 * i;          // row inside the tile
       int row;
-      const char *ksrc, *vsrc;
-      if (t < npt) {
-        // last, partial prefix tile: rows past the end repeat the last row
-        row = p0 + min(t * TK + lr, plen - 1);
-        ksrc = kc;
-        vsrc = vc;
-      } else {
-        const int bt = t - npt;
-        if constexpr (RET) {
-          row = 0;
+      if constexpr (RET) {
+        row = 0;
 #pragma unroll
-          for (int k = 0; k < NBT; ++k)
-            if (k == bt) row = brow[k][i];
-        } else {
-          row = rbase + min(bt * TK + lr, nq - 1);
-        }
-        ksrc = kb;
-        vsrc = vb;
+        for (int k = 0; k < NBT; ++k)
+          if (k == bt) row = brow[k][i];
+      } else {
+        row = rbase + min(bt * TK + lr, nq - 1);
       }
-      // koff/voff hold lr * rowstride; take it back out in integers
       const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
       char* dst = st + (2 * wave + i) * 1024;
-      dma16(ksrc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
-      if constexpr (WO) dma16(vsrc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
+      dma16(kb + (size_t)((ptrdiff_t)koff[i] + shift), dst);
+      if constexpr (WO) dma16(vb + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
     }
   };
 
@@ -276,8 +339,9 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   }
 
   // Prologue: tiles 0 .. NSTAGE-2 in flight. All index and Q loads are
-  // consumed first so that vmcnt below counts ring loads only.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // consumed first so that vmcnt below counts ring loads only (the builtin,
+  // so that the compiler knows they are complete too).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   for (int t = 0; t < NSTAGE - 1 && t < nt; ++t) issue_tile(t);
 
   f32x16 oacc[4];
@@ -549,15 +613,27 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
     order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
 }
 
-template <bool RET, bool WO>
+template <bool RET, bool WO, bool PAGED>
 hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(kThreads);
   switch (nbt) {
-    case 1: hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO>), grid, block, 0, s, a); break;
+    case 1:
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED>), grid, block, 0, s, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED>), grid, block, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED>), grid, block, 0, s, a);
+      break;
   }
   return hipGetLastError();
+}
+
+template <bool RET, bool WO>
+hipError_t launch_layout(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
+  if (a.page_table != nullptr) return launch_nbt<RET, WO, true>(nbt, batch, a, s);
+  return launch_nbt<RET, WO, false>(nbt, batch, a, s);
 }
 
 int block_tiles(int rows) {
@@ -582,12 +658,12 @@ hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
 }
 
 hipError_t launch_block_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
-  if (a.out == nullptr) return launch_nbt<false, false>(block_tiles(a.B), batch, a, s);
-  return launch_nbt<false, true>(block_tiles(a.B), batch, a, s);
+  if (a.out == nullptr) return launch_layout<false, false>(block_tiles(a.B), batch, a, s);
+  return launch_layout<false, true>(block_tiles(a.B), batch, a, s);
 }
 
 hipError_t launch_retained_attn_bf16(int batch, const AttnArgs& a, hipStream_t s) {
-  return launch_nbt<true, true>(block_tiles(a.rph), batch, a, s);
+  return launch_layout<true, true>(block_tiles(a.rph), batch, a, s);
 }
 
 }  // namespace focus

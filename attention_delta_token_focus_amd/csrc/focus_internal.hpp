@@ -41,16 +41,24 @@ struct AttnArgs {
   int hpw;                // query heads per workgroup
   int n_hc;               // head chunks per KV head
   float sl2;              // softmax scale * log2(e)
+  // Paged prefix KV (page_table non-null): k_cache / v_cache are pools of
+  // pages of page_size tokens ([pages, page_size, Hkv, d]); token t of
+  // sequence b sits in page page_table[b * pages_per_seq + t / page_size],
+  // slot t % page_size. cu_prefix then only gives the lengths.
+  const int32_t* page_table;
+  int page_size;          // a multiple of 32
+  int pages_per_seq;
 };
+
+// Heads per token are bounded so that a 32-token tile of one KV head spans
+// less than 4 GiB and in-tile byte offsets fit 32 bits.
+constexpr int kMaxHeads = 4096;
 
 // Workgroups are dispatched to the 8 XCDs of an MI355X round-robin by
 // block index, and each XCD has its own L2. The attention grid therefore
 // keeps the n_hc query-head chunks of one (sequence, KV head) item -- which
 // all stream the same K/V -- on one XCD: item i goes to XCD i % 8, and its
 // chunks are consecutive in that XCD's dispatch order.
-// Heads per token are bounded so that a 32-token tile of one KV head spans
-// less than 4 GiB and in-tile byte offsets fit 32 bits.
-constexpr int kMaxHeads = 4096;
 constexpr int kXcds = 8;
 
 __host__ __device__ inline unsigned attn_grid_size(int items, int n_hc) {

@@ -175,6 +175,101 @@ def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
     }
 
 
+def paged_pool(kv, cu, page_size, seed):
+    """The same prefix rows in shuffled pages of page_size tokens (one
+    gather on the device). Returns pool, page_table, pages_per_seq."""
+    lens = np.diff(cu)
+    need = (lens + page_size - 1) // page_size
+    pps = int(max(need.max(), 1))
+    total = int(need.sum())
+    perm = np.random.default_rng(seed).permutation(total).astype(np.int64)
+    table = np.full((len(lens), pps), -1, dtype=np.int32)
+    first = np.concatenate([[0], np.cumsum(need)[:-1]])
+    dst = np.empty(int(lens.sum()), dtype=np.int64)
+    for b, n in enumerate(lens):
+        pages = perm[first[b]:first[b] + need[b]]
+        table[b, :need[b]] = pages
+        t = np.arange(n)
+        dst[cu[b]:cu[b + 1]] = pages[t // page_size] * page_size + t % page_size
+    pool = torch.zeros((total * page_size,) + tuple(kv.shape[1:]), dtype=kv.dtype,
+                       device=kv.device)
+    pool[torch.as_tensor(dst, device=kv.device)] = kv
+    return pool, torch.as_tensor(table, device=kv.device), pps
+
+
+def time_paged(cfg, inp, dims, args, plen, page_size=64):
+    """Block attention of layer 0 over the same prefix KV held in shuffled
+    pages of 64 tokens (focus_block_attn_importance_paged), timed like the
+    packed call."""
+    import attention_delta_token_focus_amd as F
+    from attention_delta_token_focus_amd.step import FocusStep
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=0)
+    cu = np.asarray(inp.cu_prefix, dtype=np.int64)
+    L = inp.layers[0]
+    kp, table, pps = paged_pool(L["k_cache"], cu, page_size, 7)
+    vp, _, _ = paged_pool(L["v_cache"], cu, page_size, 7)
+    step.schedule()
+
+    def call():
+        F.focus_block_attn_importance_paged(
+            F.dtype_code(dims.dtype), dims.batch, dims.block, dims.hq, dims.hkv,
+            dims.head_dim, 0.0, L["q"], L["k_blk"], L["v_blk"], kp, vp, table,
+            page_size, pps, step.cu_prefix, step.order, step.max_prefix,
+            step.out[0], step.imp[0], None, step.ws, step.ws_bytes)
+
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    b = attn_bytes(cfg, plen)
+    del kp, vp
+    return {"page_size": page_size, "block_attn_us": round(us, 2),
+            "achieved_GBs": round(b / (us / 1e6) / 1e9, 1)}
+
+
+def time_masked_select(cfg, inp, dims, n_further, args):
+    """focus_select_masked with seeded still-masked flags and both
+    structural rules (selection + compaction), then the retained attention
+    of the further layers on the constrained retained set; the block
+    attention of layers 0 and 1 runs once beforehand."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    masked = workloads.draw_masked(cfg, args.seed)
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=n_further,
+                     masked=masked, rules=3)
+    layers = inp.layers
+    step.run(layers)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        step.select()
+        ev[s][1].record(stream)
+        for i, lay in enumerate(layers[2:2 + n_further]):
+            step.retained(lay, i)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    sel = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    ret = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    n_ret = int(step.cu_ret[-1].item())
+    return {
+        "select_masked_us": round(sel, 2),
+        "retained_attn_all_further_layers_us": round(ret, 2),
+        "retained_tokens": n_ret,
+        "masked_fraction": round(float(masked.mean()), 4),
+        "rules": "predecessor + masked prefix",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,8 +366,13 @@ def main() -> int:
 
     variants = None
     if not args.no_variants:
-        variants = {"layer1_importance_only": time_l1_importance_only(
-            cfg, inp, dims, n_further, args, plen)}
+        variants = {
+            "layer1_importance_only": time_l1_importance_only(
+                cfg, inp, dims, n_further, args, plen),
+            "masked_candidates_structural_rules": time_masked_select(
+                cfg, inp, dims, n_further, args),
+            "paged_prefix_kv": time_paged(cfg, inp, dims, args, plen),
+        }
 
     traffic = load_traffic(cfg.name)
     result = {

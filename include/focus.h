@@ -138,6 +138,36 @@ focus_status focus_block_attn_importance(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * focus_block_attn_importance over a paged prefix KV cache: the same
+ * computation and outputs (bit for bit), with the prefix keys/values held
+ * in fixed-size pages, the cache form of the serving engine the pages'
+ * system is built into (LMDeploy: Pith page, Referee Report; PagedAttention
+ * is listed among the works it builds on on the mlsanity page, "Builds
+ * on").
+ *
+ *  k_pages, v_pages  [n_pages, page_size, Hkv, d] page pools (type dt).
+ *  page_table  device int32 [batch, pages_per_seq]: token t of sequence b
+ *              is slot t % page_size of page page_table[b][t / page_size].
+ *              Entries past a sequence's last page are not read.
+ *  page_size   tokens per page, a positive multiple of 32.
+ *  pages_per_seq  row stride of page_table; pages_per_seq * page_size
+ *              must cover max_prefix.
+ *  cu_prefix   as above; only the lengths cu_prefix[b+1] - cu_prefix[b]
+ *              are used.
+ * Other arguments as focus_block_attn_importance.
+ * Errors: as focus_block_attn_importance, plus UNSUPPORTED for a page_size
+ * that is not a positive multiple of 32 and INVALID_ARG for a NULL
+ * page_table (max_prefix > 0) or pages that cannot hold max_prefix.
+ */
+focus_status focus_block_attn_importance_paged(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk,
+    const void* k_pages, const void* v_pages, const int32_t* page_table,
+    int page_size, int pages_per_seq, const int32_t* cu_prefix,
+    const int32_t* order, int max_prefix, void* out, float* imp, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Head mean, MaxPool1D smoothing, importance delta and per-sequence top-K.
  *
  * Follows the Pith page, "What carries the argument": the importance is
@@ -274,6 +304,20 @@ focus_status focus_retained_attn(
     const void* q_src, const void* k_src, const void* v_src,
     const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
+    const int32_t* order, int max_prefix, void* out, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
+ * focus_retained_attn over a paged prefix KV cache (layout and page
+ * arguments as in focus_block_attn_importance_paged); same outputs, bit
+ * for bit.
+ */
+focus_status focus_retained_attn_paged(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q_src, const void* k_src, const void* v_src,
+    const int32_t* idx, const int32_t* cu_ret, int n_ret, int max_ret,
+    const void* k_pages, const void* v_pages, const int32_t* page_table,
+    int page_size, int pages_per_seq, const int32_t* cu_prefix,
     const int32_t* order, int max_prefix, void* out, void* workspace,
     size_t workspace_bytes, void* stream);
 

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(F.lib, name), name
         assert callable(getattr(F, name)), name
@@ -82,6 +82,46 @@ def _attn(**kw):
 def test_block_attention_rejects_bad_arguments(kw, code):
     assert _attn(**kw) == code
     assert F.focus_last_error().startswith("focus_block_attn_importance")
+
+
+def _paged(**kw):
+    a = dict(dt=1, batch=2, B=32, Hq=32, Hkv=8, d=128, scale=0.0, q=FAKE,
+             k_blk=FAKE, v_blk=FAKE, k_pages=FAKE, v_pages=FAKE, table=FAKE,
+             page_size=64, pps=4, cu_prefix=FAKE, order=None, max_prefix=256,
+             out=FAKE, imp=FAKE, lse=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return F.lib.focus_block_attn_importance_paged(
+        a["dt"], a["batch"], a["B"], a["Hq"], a["Hkv"], a["d"], a["scale"],
+        a["q"], a["k_blk"], a["v_blk"], a["k_pages"], a["v_pages"], a["table"],
+        a["page_size"], a["pps"], a["cu_prefix"], a["order"], a["max_prefix"],
+        a["out"], a["imp"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=0), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(page_size=48), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(page_size=16), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(pps=3), F.FOCUS_ERR_INVALID_ARG),
+    (dict(pps=-1), F.FOCUS_ERR_INVALID_ARG),
+    (dict(table=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(table=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),
+    (dict(k_pages=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(batch=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(d=96), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(ws=None, ws_bytes=0), F.FOCUS_ERR_WORKSPACE),
+])
+def test_paged_block_attention_rejects_bad_arguments(kw, code):
+    assert _paged(**kw) == code
+    assert F.focus_last_error().startswith("focus_block_attn_importance_paged")
+
+
+def test_paged_retained_attention_checks_pages():
+    args = [1, 2, 32, 32, 8, 128, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 5,
+            FAKE, FAKE, FAKE, 64, 1, FAKE, None, 256, FAKE, None, 0, None]
+    assert F.lib.focus_retained_attn_paged(*args) == F.FOCUS_ERR_INVALID_ARG
+    assert "pages_per_seq" in F.focus_last_error()
+    args[17] = 40
+    assert F.lib.focus_retained_attn_paged(*args) == F.FOCUS_ERR_UNSUPPORTED
 
 
 def _topk(**kw):

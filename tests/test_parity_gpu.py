@@ -49,6 +49,11 @@ def test_c5_reduced_batch_several_layers():
     _case("c5 reduced", cfg)
 
 
+def test_c6_b64_reduced_batch():
+    cfg = workloads.scaled(workloads.get("c6"), batch=16)
+    _case("c6 reduced", cfg, n_layers=3)
+
+
 EDGE = [
     # name, overrides, prefix lengths, budgets
     ("B1 P0/1/63 d64", dict(block=1, hq=4, hkv=1, head_dim=64), [0, 1, 63], [0, 1, 1]),
@@ -271,3 +276,83 @@ def test_masked_select_without_mask_or_rules_equals_focus_select():
     assert torch.equal(dI.cpu(), torch.from_numpy(r1["dI"]))
     assert torch.equal(cu.cpu(), torch.from_numpy(r1["cu_ret"]))
     assert np.array_equal(idx.cpu().numpy()[:step.n_ret], r1["idx"])
+
+
+def _paged_pool(kv, cu, page_size, seed, slack=3):
+    """The same prefix rows scattered over shuffled pages of a NaN-filled
+    pool (a wrong read shows up as NaN). Returns pool, page_table,
+    pages_per_seq."""
+    lens = np.diff(cu)
+    need = [(int(n) + page_size - 1) // page_size for n in lens]
+    pps = max(max(need), 1)
+    total = sum(need) + slack
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(total)
+    pool = torch.full((total * page_size,) + tuple(kv.shape[1:]), float("nan"),
+                      dtype=kv.dtype, device=kv.device)
+    table = np.full((len(lens), pps), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(lens):
+        for p in range(need[b]):
+            pg = int(perm[k])
+            k += 1
+            table[b, p] = pg
+            lo = int(cu[b]) + p * page_size
+            hi = min(int(cu[b + 1]), lo + page_size)
+            pool[pg * page_size:pg * page_size + hi - lo] = kv[lo:hi]
+    return pool.contiguous(), torch.as_tensor(table, device=kv.device), pps
+
+
+PAGED = [
+    ("c3 B32 pages of 64", dict(), None, 64),
+    ("c3 B32 pages of 32", dict(), None, 32),
+    ("B128 pages of 128", dict(block=128, pool_k=5), [100, 0, 2100], 128),
+    ("B7 ragged pages of 96", dict(block=7), [5, 90, 1, 0, 200], 96),
+    ("f32 d64 pages of 64", dict(dtype="f32", head_dim=64, hq=4, hkv=1), [70, 3, 130], 64),
+]
+
+
+@pytest.mark.parametrize("name,over,plens,ps", PAGED, ids=[p[0] for p in PAGED])
+def test_paged_prefix_equals_packed(name, over, plens, ps):
+    """Paged prefix KV: block attention (with and without O) and retained
+    attention are bitwise those of the packed layout, which the other tests
+    compare with the oracle; the packed results are re-checked here too."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 12,
+                           **over)
+    log(f"[parity] paged {name}: N={cfg.batch} B={cfg.block} page_size={ps}")
+    inp = workloads.make_inputs(cfg, 31, n_layers=3, prefix_lens=plens)
+    lay = parity.to_device(inp)
+    step, res = parity.run_gpu(inp, layers_dev=lay)
+    parity.compare_step(inp, res, range(cfg.batch))
+    dm = step.dims
+    cu = np.asarray(inp.cu_prefix, dtype=np.int64)
+    for li, which in ((0, "block"), (1, "imp_only"), (2, "retained")):
+        L = lay[li]
+        kp, table, pps = _paged_pool(L["k_cache"], cu, ps, 100 + li)
+        vp, table_v, _ = _paged_pool(L["v_cache"], cu, ps, 100 + li)
+        assert torch.equal(table, table_v)
+        if which == "retained":
+            out = torch.empty_like(step.ret_out[0])
+            F.focus_retained_attn_paged(
+                F.dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
+                dm.head_dim, 0.0, L["q"], L["k_blk"], L["v_blk"], step.idx,
+                step.cu_ret, step.n_ret, step.max_ret, kp, vp, table, ps, pps,
+                step.cu_prefix, step.order, step.max_prefix, out, step.ws,
+                step.ws_bytes)
+            torch.cuda.synchronize()
+            assert torch.equal(out[:step.n_ret], step.ret_out[0][:step.n_ret])
+            continue
+        with_out = which == "block"
+        out = torch.empty_like(step.out[0]) if with_out else None
+        imp = torch.empty_like(step.imp[0])
+        lse = torch.empty_like(step.lse[0])
+        F.focus_block_attn_importance_paged(
+            F.dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv, dm.head_dim,
+            0.0, L["q"], L["k_blk"], L["v_blk"] if with_out else None,
+            kp, vp if with_out else None, table, ps, pps, step.cu_prefix,
+            step.order, step.max_prefix, out, imp, lse, step.ws, step.ws_bytes)
+        torch.cuda.synchronize()
+        assert torch.equal(imp, step.imp[li]) and torch.equal(lse, step.lse[li])
+        if with_out:
+            assert torch.equal(out, step.out[li])

@@ -1,4 +1,4 @@
-"""The five seeded synthetic workloads of the FOCUS eviction hot path.
+"""The seeded synthetic workloads of the FOCUS eviction hot path.
 
 Shapes follow the block-diffusion setting reviewed on the pith.science page
 for "FOCUS: DLLMs Know How to Tame Their Compute Bound" (arXiv 2601.23278):
@@ -68,6 +68,14 @@ CONFIGS = {
         block=32, hq=32, hkv=8, head_dim=128, dtype="bf16", pool_k=3,
         prefix_lognormal=(2048.0, 0.8, 256, 8192), budget_fixed=0.30,
         planted_fixed=0.10, extra_layers=34),
+    # Block size 64, the setting of the pages' largest speed-up (Fig. 7,
+    # per the Pith page's Referee Report; B = 64 also in Fig. 9); otherwise
+    # shaped like c3.
+    "c6": FocusConfig(
+        name="c6_bf16_n128_b64_lognormal1024", index=6, batch=128, block=64,
+        hq=32, hkv=8, head_dim=128, dtype="bf16", pool_k=3,
+        prefix_lognormal=(1024.0, 0.8, 128, 4096),
+        budget_uniform=(0.20, 0.35), planted_uniform=(0.05, 0.20)),
 }
 
 
