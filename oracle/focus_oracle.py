@@ -36,7 +36,8 @@ same paper, cited as "ScienceStack page"):
 Readings where the pages are silent are listed in the design notes of the
 repository; the ones that change numbers are: scale 1/sqrt(d) unless given,
 GQA head h uses KV head h // (Hq/Hkv), the head aggregation is the mean,
-MaxPool pads with -inf, ties in top-K go to the lower index.
+MaxPool pads with -inf, ties in top-K go to the lower index. The dynamic
+budget (dynamic_budget) is a labelled reading whose parity is unpinned.
 
 Inputs may be float32 arrays holding bf16 values (exact); every slice is
 widened to float64 before any arithmetic.
@@ -199,6 +200,36 @@ def select_constrained(d_imp: np.ndarray, masked: np.ndarray, k_keep,
                 if masked[b, j]:
                     keep[b, j] = 1
     return keep, cand
+
+
+def dynamic_budget(d_imp: np.ndarray, masked: np.ndarray, yield_hist,
+                   alpha: float = 1.5) -> np.ndarray:
+    """A reading of the dynamic budget (parity unpinned: the pages name its
+    inputs but do not print the formula). The Pith page's summary sets the
+    budget from the historical decoding yield and within-block delta
+    statistics; Eq. 4's expansion factor alpha (default 1.5, Free-Parameter
+    Ledger) scales it; Fig. 14 marks a +Std threshold on the delta.
+
+    Read here, per sequence b over its masked positions M (all if masked is
+    None): mu and sigma are the mean and population standard deviation of
+    dI over M; n = #{j in M : dI_j > mu + sigma}; y = yield_hist[b];
+    K_b = min(|M|, max(1, ceil(alpha * max(y, n)))), and 0 when M is empty.
+    Returns K [N] int64."""
+    d_imp = np.asarray(d_imp, dtype=F64)
+    n_seq, blk = d_imp.shape
+    m = (np.ones((n_seq, blk), dtype=bool) if masked is None
+         else np.asarray(masked).astype(bool))
+    k = np.zeros(n_seq, dtype=np.int64)
+    for b in range(n_seq):
+        vals = [float(d_imp[b, j]) for j in range(blk) if m[b, j]]
+        if not vals:
+            continue
+        mu = sum(vals) / len(vals)
+        sigma = math.sqrt(sum((v - mu) ** 2 for v in vals) / len(vals))
+        above = sum(1 for v in vals if v > mu + sigma)
+        want = math.ceil(alpha * max(float(yield_hist[b]), float(above)))
+        k[b] = min(len(vals), max(1, want))
+    return k
 
 
 def compact(keep: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -103,3 +103,48 @@ def test_all_masked_with_prefix_rule_keeps_a_contiguous_head():
 def test_nothing_masked_retains_nothing():
     keep, cand = oracle.select_constrained(np.ones((2, 8)), np.zeros((2, 8)), [3, 8])
     assert keep.sum() == 0 and cand.sum() == 0
+
+
+# ------------------------------------------------------------ dynamic budget
+def _budget_cases():
+    return golden_io.load("dynamic_budget.json")
+
+
+@pytest.mark.parametrize("case", _budget_cases()["cases"], ids=lambda c: c["name"])
+def test_golden_dynamic_budget(case):
+    alpha = float(golden_io.arr(_budget_cases()["alpha"]))
+    k = oracle.dynamic_budget(golden_io.arr(case["dI"])[None, :],
+                              np.array(case["masked"])[None, :],
+                              [float(golden_io.arr(case["yield"]))], alpha)
+    assert int(k[0]) == case["expect_k"]
+
+
+def test_dynamic_budget_against_numpy_statistics():
+    """The same reading through numpy's mean / std (ddof 0) on random
+    inputs, and its bounds."""
+    rng = np.random.default_rng(11)
+    n, blk = 50, 32
+    dI = rng.standard_normal((n, blk))
+    masked = (rng.random((n, blk)) < 0.6).astype(np.uint8)
+    y = rng.integers(0, 12, n) / 2.0
+    k = oracle.dynamic_budget(dI, masked, y, 1.5)
+    for b in range(n):
+        v = dI[b][masked[b] == 1]
+        if v.size == 0:
+            assert k[b] == 0
+            continue
+        above = int((v > v.mean() + v.std()).sum())
+        want = min(v.size, max(1, int(np.ceil(1.5 * max(y[b], above)))))
+        assert k[b] == want
+        assert 1 <= k[b] <= v.size
+
+
+def test_dynamic_budget_grows_with_alpha_and_history():
+    rng = np.random.default_rng(12)
+    dI = rng.standard_normal((20, 32))
+    masked = np.ones((20, 32), dtype=np.uint8)
+    y = np.full(20, 3.0)
+    k1 = oracle.dynamic_budget(dI, masked, y, 1.2)
+    k2 = oracle.dynamic_budget(dI, masked, y, 1.8)
+    k3 = oracle.dynamic_budget(dI, masked, y + 4, 1.8)
+    assert (k1 <= k2).all() and (k2 <= k3).all() and (k3 > k1).any()

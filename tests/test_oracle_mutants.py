@@ -39,6 +39,7 @@ PINS = [
     PC.test_all_masked_without_constraints_is_plain_topk,
     PC.test_all_masked_with_prefix_rule_keeps_a_contiguous_head,
     PC.test_nothing_masked_retains_nothing,
+    *[(lambda c=c: PC.test_golden_dynamic_budget(c)) for c in PC._budget_cases()["cases"]],
 ]
 
 # (name, [(old, new, occurrence)])
@@ -96,11 +97,22 @@ MUTANTS = [
                                             "key=lambda j: (-d_imp[b, j], -j)", 1)]),
     ("constrained: smallest deltas", [("key=lambda j: (-d_imp[b, j], j)",
                                        "key=lambda j: (d_imp[b, j], j)", 1)]),
+    ("budget: sample std", [("sum((v - mu) ** 2 for v in vals) / len(vals)",
+                             "sum((v - mu) ** 2 for v in vals) / max(len(vals) - 1, 1)", 0)]),
+    ("budget: threshold inclusive", [("if v > mu + sigma", "if v >= mu + sigma", 0)]),
+    ("budget: floor", [("want = math.ceil(", "want = math.floor(", 0)]),
+    ("budget: yield plus count", [("max(float(yield_hist[b]), float(above))",
+                                   "(float(yield_hist[b]) + float(above))", 0)]),
+    ("budget: decoded positions counted", [(
+        "vals = [float(d_imp[b, j]) for j in range(blk) if m[b, j]]",
+        "vals = [float(d_imp[b, j]) for j in range(blk)]", 0)]),
+    ("budget: no floor of one", [("k[b] = min(len(vals), max(1, want))",
+                                  "k[b] = min(len(vals), want)", 0)]),
 ]
 
 EXPORTED = ["attention_rows", "block_attn_importance", "block_step", "compact",
             "default_scale", "head_mean_maxpool", "importance_delta",
-            "retained_attn", "select_constrained", "topk_keep"]
+            "retained_attn", "select_constrained", "topk_keep", "dynamic_budget"]
 
 
 def _replace_nth(src, old, new, n):
