@@ -68,6 +68,9 @@ _SIGS = {
     "focus_select": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "focus_select_masked": (
         _I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]),
+    "focus_select_dynamic": (
+        _I, [_I, _I, _I, _I, _P, _P, _P, _P, _c.c_float, _I, _P, _P, _P, _P, _P,
+             _P, _P]),
     "focus_retained_attn_workspace": (
         _I, [_I, _I, _I, _I, _I, _I, _I, _c.POINTER(_SZ)]),
     "focus_retained_attn": (
@@ -212,6 +215,17 @@ def focus_select_masked(batch, B, Hq, pool_k, imp0, imp1, masked, k_keep,
     _check(lib.focus_select_masked(
         batch, B, Hq, pool_k, _ptr(imp0, "imp0"), _ptr(imp1, "imp1"),
         _ptr(masked, "masked", True), _ptr(k_keep, "k_keep"), int(rules),
+        _ptr(keep, "keep"), _ptr(cand, "cand", True), _ptr(dI, "dI", True),
+        _ptr(idx, "idx", True), _ptr(cu_ret, "cu_ret", True), _stream(stream)))
+
+
+def focus_select_dynamic(batch, B, Hq, pool_k, imp0, imp1, masked, yield_hist,
+                         alpha, rules, keep, k_used=None, cand=None, dI=None,
+                         idx=None, cu_ret=None, stream=None) -> None:
+    _check(lib.focus_select_dynamic(
+        batch, B, Hq, pool_k, _ptr(imp0, "imp0"), _ptr(imp1, "imp1"),
+        _ptr(masked, "masked", True), _ptr(yield_hist, "yield_hist"),
+        float(alpha), int(rules), _ptr(k_used, "k_used", True),
         _ptr(keep, "keep"), _ptr(cand, "cand", True), _ptr(dI, "dI", True),
         _ptr(idx, "idx", True), _ptr(cu_ret, "cu_ret", True), _stream(stream)))
 

@@ -362,8 +362,8 @@ focus_status focus_delta_topk(int batch, int B, int Hq, int pool_k,
     if (k_keep == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: k_keep is NULL", fn);
     if (keep == nullptr) return fail(FOCUS_ERR_INVALID_ARG, "%s: keep is NULL", fn);
     return hip_status(focus::launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1, nullptr,
-                                               0, k_keep, keep, nullptr, dI,
-                                               (hipStream_t)stream),
+                                               0, k_keep, nullptr, 0.f, nullptr, keep,
+                                               nullptr, dI, (hipStream_t)stream),
                       "delta/top-K launch");
   } catch (...) {
     return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
@@ -419,8 +419,46 @@ focus_status focus_select_masked(int batch, int B, int Hq, int pool_k,
       return fail(FOCUS_ERR_INVALID_ARG, "%s: idx and cu_ret must be both given or both NULL",
                   fn);
     hipError_t e = focus::launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1, masked, rules,
-                                            k_keep, keep, cand, dI, (hipStream_t)stream);
+                                            k_keep, nullptr, 0.f, nullptr, keep, cand, dI,
+                                            (hipStream_t)stream);
     if (e != hipSuccess || idx == nullptr) return hip_status(e, "masked delta/top-K launch");
+    return hip_status(focus::launch_compact(batch, B, keep, idx, cu_ret, (hipStream_t)stream),
+                      "compaction launch");
+  } catch (...) {
+    return fail(FOCUS_ERR_HIP, "%s: unexpected host exception", fn);
+  }
+}
+
+focus_status focus_select_dynamic(int batch, int B, int Hq, int pool_k,
+                                  const float* imp0, const float* imp1,
+                                  const uint8_t* masked, const float* yield_hist,
+                                  float alpha, int rules, int32_t* k_used,
+                                  uint8_t* keep, uint8_t* cand, float* dI,
+                                  int32_t* idx, int32_t* cu_ret, void* stream) {
+  const char* fn = "focus_select_dynamic";
+  try {
+    if (batch < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: batch %d < 1", fn, batch);
+    if (B < 1 || B > 128)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: B %d outside [1, 128]", fn, B);
+    if (Hq < 1) return fail(FOCUS_ERR_INVALID_ARG, "%s: Hq %d < 1", fn, Hq);
+    if (pool_k < 1 || pool_k > 255 || pool_k % 2 == 0)
+      return fail(FOCUS_ERR_UNSUPPORTED, "%s: pool_k %d must be odd in [1, 255]",
+                  fn, pool_k);
+    if (rules & ~(FOCUS_KEEP_PREDECESSOR | FOCUS_KEEP_MASKED_PREFIX))
+      return fail(FOCUS_ERR_UNSUPPORTED, "%s: unknown rule bits 0x%x", fn, rules);
+    if (!(alpha > 0.f) || !(alpha < 1e6f))
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: alpha %g outside (0, 1e6)", fn, (double)alpha);
+    REQUIRE_PTR(imp0);
+    REQUIRE_PTR(imp1);
+    if (yield_hist == nullptr || keep == nullptr)
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: yield_hist and keep must be non-NULL", fn);
+    if ((idx == nullptr) != (cu_ret == nullptr))
+      return fail(FOCUS_ERR_INVALID_ARG, "%s: idx and cu_ret must be both given or both NULL",
+                  fn);
+    hipError_t e = focus::launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1, masked, rules,
+                                            nullptr, yield_hist, alpha, k_used, keep, cand,
+                                            dI, (hipStream_t)stream);
+    if (e != hipSuccess || idx == nullptr) return hip_status(e, "dynamic delta/top-K launch");
     return hip_status(focus::launch_compact(batch, B, keep, idx, cu_ret, (hipStream_t)stream),
                       "compaction launch");
   } catch (...) {

@@ -92,8 +92,9 @@ size_t order_workspace_bytes(int batch);
 hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
                              const uint8_t* masked, int rules,
-                             const int32_t* k_keep, uint8_t* keep, uint8_t* cand,
-                             float* dI, hipStream_t s);
+                             const int32_t* k_keep, const float* yield_hist,
+                             float alpha, int32_t* k_used, uint8_t* keep,
+                             uint8_t* cand, float* dI, hipStream_t s);
 hipError_t launch_select(int batch, int B, int Hq, int pool_k,
                          const float* imp0, const float* imp1,
                          const int32_t* k_keep, uint8_t* keep, float* dI,

@@ -87,21 +87,40 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&key)[2], int lane) {
 // (kKeepPredecessor) and every masked position left of the rightmost
 // candidate (kKeepMaskedPrefix). `cand`, when given, receives the
 // candidate flags. Without a mask and rules this is plain top-K.
+//
+// With `yield_hist` given, the budget is not k_keep[b] but the dynamic
+// budget K = min(|M|, max(1, ceil(alpha * max(y_b, n)))), n = the masked
+// positions whose delta exceeds mean + population std of the deltas over
+// the masked positions (0 if none is masked); it is written to k_used[b]
+// when k_used is given. Sums are fixed-order wavefront reductions in fp32.
 constexpr int kKeepPredecessor = 1;
 constexpr int kKeepMaskedPrefix = 2;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
 template <int NS>
 __device__ __forceinline__ void delta_topk_wave(
     int b, int B, int Hq, int radius, const float* __restrict__ imp0,
     const float* __restrict__ imp1, const uint8_t* __restrict__ masked,
-    int rules, const int32_t* __restrict__ k_keep, uint8_t* __restrict__ keep,
+    int rules, const int32_t* __restrict__ k_keep,
+    const float* __restrict__ yield_hist, float alpha,
+    int32_t* __restrict__ k_used, uint8_t* __restrict__ keep,
     uint8_t* __restrict__ cand, float* __restrict__ dI, float (*mean)[128],
     uint8_t* flags, int& n_kept) {
   const int lane = threadIdx.x;
   const float inv_h = 1.0f / (float)Hq;
   const float* i0 = imp0 + (size_t)b * Hq * B;
   const float* i1 = imp1 + (size_t)b * Hq * B;
-  const int kb = min(max(k_keep[b], 0), B);
+  int kb = yield_hist != nullptr ? 0 : min(max(k_keep[b], 0), B);
   bool elig[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -121,9 +140,11 @@ __device__ __forceinline__ void delta_topk_wave(
   // first and, for equal dI, the lower position. Empty slots and positions
   // that are not candidates are 0, below every real key (~j is never 0).
   uint64_t key[2] = {0, 0};
+  float dv[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = lane + 64 * s;
+    dv[s] = 0.f;
     if (j < B) {
       const int lo = max(0, j - radius), hi = min(B - 1, j + radius);
       float m0 = -INFINITY, m1 = -INFINITY;
@@ -132,9 +153,41 @@ __device__ __forceinline__ void delta_topk_wave(
         m1 = fmaxf(m1, mean[1][t]);
       }
       const float d = m1 - m0;
+      dv[s] = d;
       if (dI != nullptr) dI[(size_t)b * B + j] = d;
       if (elig[s]) key[s] = ((uint64_t)order_code(d) << 32) | (uint32_t)(0xFFFFFFFFu - j);
     }
+  }
+  if (yield_hist != nullptr) {
+    // dynamic budget from the masked positions' delta statistics
+    float sum = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (elig[s]) {
+        sum += dv[s];
+        ++cnt;
+      }
+    }
+    sum = wave_sum(sum);
+    cnt = wave_sum(cnt);
+    if (cnt > 0) {
+      const float mu = sum / (float)cnt;
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (elig[s]) ss += (dv[s] - mu) * (dv[s] - mu);
+      }
+      ss = wave_sum(ss);
+      const float thr = mu + __builtin_sqrtf(ss / (float)cnt);
+      int above = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) above += (elig[s] && dv[s] > thr) ? 1 : 0;
+      above = wave_sum(above);
+      const float want = __builtin_ceilf(alpha * fmaxf(yield_hist[b], (float)above));
+      kb = min(cnt, max(1, (int)fminf(want, (float)B)));
+    }
+    if (k_used != nullptr && lane == 0) k_used[b] = kb;
   }
   bitonic_desc<NS>(key, lane);
   // Candidates: the first K_b ranks that hold a real key.
@@ -190,13 +243,14 @@ template <int NS>
 __global__ void __launch_bounds__(64) delta_topk_kernel(
     int B, int Hq, int radius, const float* __restrict__ imp0,
     const float* __restrict__ imp1, const uint8_t* __restrict__ masked,
-    int rules, const int32_t* __restrict__ k_keep, uint8_t* __restrict__ keep,
-    uint8_t* __restrict__ cand, float* __restrict__ dI) {
+    int rules, const int32_t* __restrict__ k_keep,
+    const float* __restrict__ yield_hist, float alpha, int32_t* __restrict__ k_used,
+    uint8_t* __restrict__ keep, uint8_t* __restrict__ cand, float* __restrict__ dI) {
   __shared__ float mean[2][128];
   __shared__ uint8_t flags[128];
   int n_kept;
   delta_topk_wave<NS>(blockIdx.x, B, Hq, radius, imp0, imp1, masked, rules, k_keep,
-                      keep, cand, dI, mean, flags, n_kept);
+                      yield_hist, alpha, k_used, keep, cand, dI, mean, flags, n_kept);
 }
 
 // Delta/top-K and compaction in one launch, one wavefront per sequence.
@@ -222,8 +276,8 @@ __global__ void __launch_bounds__(64) select_kernel(
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
   int kb;
-  delta_topk_wave<NS>(b, B, Hq, radius, imp0, imp1, nullptr, 0, k_keep, keep,
-                      nullptr, dI, mean, flags, kb);
+  delta_topk_wave<NS>(b, B, Hq, radius, imp0, imp1, nullptr, 0, k_keep, nullptr,
+                      0.f, nullptr, keep, nullptr, dI, mean, flags, kb);
   int base = off;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -334,16 +388,17 @@ __global__ void __launch_bounds__(1024) compact_kernel(
 hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const float* imp0, const float* imp1,
                              const uint8_t* masked, int rules,
-                             const int32_t* k_keep, uint8_t* keep, uint8_t* cand,
-                             float* dI, hipStream_t s) {
+                             const int32_t* k_keep, const float* yield_hist,
+                             float alpha, int32_t* k_used, uint8_t* keep,
+                             uint8_t* cand, float* dI, hipStream_t s) {
   if (B <= 64) {
     hipLaunchKernelGGL(delta_topk_kernel<1>, dim3(batch), dim3(64), 0, s, B, Hq,
-                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, keep,
-                       cand, dI);
+                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, yield_hist,
+                       alpha, k_used, keep, cand, dI);
   } else {
     hipLaunchKernelGGL(delta_topk_kernel<2>, dim3(batch), dim3(64), 0, s, B, Hq,
-                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, keep,
-                       cand, dI);
+                       (pool_k - 1) / 2, imp0, imp1, masked, rules, k_keep, yield_hist,
+                       alpha, k_used, keep, cand, dI);
   }
   return hipGetLastError();
 }

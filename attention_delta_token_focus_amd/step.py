@@ -28,7 +28,7 @@ from . import (dtype_code, focus_block_attn_importance,
                focus_block_attn_importance_workspace, focus_compact,
                focus_delta_topk, focus_retained_attn,
                focus_retained_attn_workspace, focus_schedule, focus_select,
-               focus_select_masked)
+               focus_select_dynamic, focus_select_masked)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -56,12 +56,15 @@ class FocusStep:
     def __init__(self, dims: Dims, cu_prefix_host: Sequence[int],
                  k_keep_host: Sequence[int], n_further: int = 0,
                  device="cuda", with_lse: bool = False, fused: bool = True,
-                 l1_output: bool = True, masked=None, rules: int = 0):
+                 l1_output: bool = True, masked=None, rules: int = 0,
+                 yield_hist=None, alpha: float = 1.5):
         self.dims = dims
         self.fused = fused
         self.l1_output = l1_output
-        self.constrained = masked is not None or rules != 0
+        self.constrained = (masked is not None or rules != 0
+                            or yield_hist is not None)
         self.rules = rules
+        self.alpha = alpha
         dv = torch.device(device)
         n, blk, hq, d = dims.batch, dims.block, dims.hq, dims.head_dim
         cu = np.asarray(cu_prefix_host, dtype=np.int64)
@@ -79,6 +82,12 @@ class FocusStep:
                 self.masked = torch.as_tensor(
                     np.asarray(masked, dtype=np.uint8), device=dv).contiguous()
             self.cand = torch.empty((n, blk), device=dv, dtype=torch.uint8)
+        self.yield_hist = None
+        self.k_used = None
+        if yield_hist is not None:
+            self.yield_hist = torch.as_tensor(
+                np.asarray(yield_hist, dtype=np.float32), device=dv).contiguous()
+            self.k_used = torch.empty((n,), device=dv, dtype=torch.int32)
         f32 = dict(device=dv, dtype=torch.float32)
         self.out = [torch.empty((n * blk, hq, d), device=dv, dtype=dims.dtype)
                     if w == 0 or l1_output else None for w in range(2)]
@@ -121,6 +130,13 @@ class FocusStep:
 
     def select(self, stream=None) -> None:
         dm = self.dims
+        if self.yield_hist is not None:
+            focus_select_dynamic(dm.batch, dm.block, dm.hq, dm.pool_k,
+                                 self.imp[0], self.imp[1], self.masked,
+                                 self.yield_hist, self.alpha, self.rules,
+                                 self.keep, self.k_used, self.cand, self.dI,
+                                 self.idx, self.cu_ret, stream)
+            return
         if self.constrained:
             focus_select_masked(dm.batch, dm.block, dm.hq, dm.pool_k,
                                 self.imp[0], self.imp[1], self.masked,

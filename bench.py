@@ -235,6 +235,33 @@ def time_paged(cfg, inp, dims, args, plen, page_size=64):
             "achieved_GBs": round(b / (us / 1e6) / 1e9, 1)}
 
 
+def time_dynamic_select(cfg, inp, dims, args):
+    """focus_select_dynamic (the labelled reading of the dynamic budget)
+    with the same still-masked flags and both structural rules."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    masked = workloads.draw_masked(cfg, args.seed)
+    y = workloads.draw_yield(cfg, args.seed)
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=0,
+                     masked=masked, rules=3, yield_hist=y, alpha=1.5)
+    step.run(inp.layers)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        step.select()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    k = step.k_used.cpu().numpy()
+    return {
+        "select_dynamic_us": round(float(np.mean(
+            [e[0].elapsed_time(e[1]) for e in ev])) * 1e3, 2),
+        "alpha": 1.5, "mean_budget": round(float(k.mean()), 3),
+        "retained_tokens": int(step.cu_ret[-1].item()),
+    }
+
+
 def time_masked_select(cfg, inp, dims, n_further, args):
     """focus_select_masked with seeded still-masked flags and both
     structural rules (selection + compaction), then the retained attention
@@ -372,6 +399,7 @@ def main() -> int:
             "masked_candidates_structural_rules": time_masked_select(
                 cfg, inp, dims, n_further, args),
             "paged_prefix_kv": time_paged(cfg, inp, dims, args, plen),
+            "dynamic_budget_reading": time_dynamic_select(cfg, inp, dims, args),
         }
 
     traffic = load_traffic(cfg.name)

@@ -272,6 +272,37 @@ focus_status focus_select_masked(int batch, int B, int Hq, int pool_k,
                                  float* dI, int32_t* idx, int32_t* cu_ret,
                                  void* stream);
 
+/*
+ * focus_select_masked with the budget set on the device from the block's
+ * own deltas and the decoding history: a READING of the pages' dynamic
+ * budgeting, whose formula the pages do not print (parity against the
+ * pages is unpinned; the oracle implements the same reading). The pages
+ * name its inputs: the historical decoding yield and within-block delta
+ * statistics (Pith page, summary), the expansion factor alpha of Eq. 4
+ * (default 1.5; Axiom & Free-Parameter Ledger) and a +Std threshold on
+ * the delta (Fig. 14 caption). Read as, per sequence b over its masked
+ * positions M (all positions if masked is NULL):
+ *    mu, sigma = mean and population std of dI over M;
+ *    n   = #{ j in M : dI[b,j] > mu + sigma };
+ *    K_b = min(|M|, max(1, ceil(alpha * max(yield_hist[b], n)))),
+ *          0 when M is empty;
+ * computed in fp32 with fixed-order reductions; then candidates, rules
+ * and compaction exactly as focus_select_masked with k_keep = K.
+ *
+ *  yield_hist  device float32 [batch]: the decoding yield history of each
+ *              sequence (e.g. tokens decoded at its previous step).
+ *  alpha       expansion factor, in (0, 1e6).
+ *  k_used      device int32 [batch] output: K_b, or NULL.
+ * Other arguments and errors as focus_select_masked, plus INVALID_ARG for
+ * a NULL yield_hist or alpha out of range.
+ */
+focus_status focus_select_dynamic(int batch, int B, int Hq, int pool_k,
+                                  const float* imp0, const float* imp1,
+                                  const uint8_t* masked, const float* yield_hist,
+                                  float alpha, int rules, int32_t* k_used,
+                                  uint8_t* keep, uint8_t* cand, float* dI,
+                                  int32_t* idx, int32_t* cu_ret, void* stream);
+
 /* Workspace bytes that focus_retained_attn needs for these sizes. */
 focus_status focus_retained_attn_workspace(
     int batch, int Hq, int Hkv, int d, int max_prefix, int n_ret,

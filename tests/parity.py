@@ -65,6 +65,8 @@ def run_gpu(inp: workloads.Inputs, layers_dev=None, n_further: Optional[int] = N
         lse=[l.cpu().numpy() if l is not None else None for l in step.lse],
         dI=step.dI.cpu().numpy(), keep=step.keep.cpu().numpy(),
         cand=step.cand.cpu().numpy() if step.cand is not None else None,
+        k_used=step.k_used.cpu().numpy() if getattr(step, "k_used", None) is not None
+        else None,
         idx=step.idx.cpu().numpy()[:step.n_ret],
         cu_ret=step.cu_ret.cpu().numpy(),
         ret=[to_f32_numpy(r)[:step.n_ret] for r in step.ret_out])
@@ -212,7 +214,8 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
     return rep
 
 
-def compare_constrained(inp: workloads.Inputs, res, masked, rules: int):
+def compare_constrained(inp: workloads.Inputs, res, masked, rules: int,
+                        k_keep=None, k_gpu=None, skip=()):
     """The masked-candidate selection with structural rules against the
     oracle's own selection on the oracle's own importance (all sequences),
     plus the retained attention of the further layers on exactly matched
@@ -232,12 +235,18 @@ def compare_constrained(inp: workloads.Inputs, res, masked, rules: int):
                      TIGHT[kind]["imp"])
     dI_ref = oracle.importance_delta(o[0][1], o[1][1], cfg.pool_k)
     assert_close("dI", res["dI"], dI_ref, TIGHT[kind]["dI"])
-    k_keep = inp.meta.k_keep
+    if k_keep is None:
+        k_keep = inp.meta.k_keep
+    if k_gpu is None:
+        k_gpu = k_keep
     keep_ref, cand_ref = oracle.select_constrained(dI_ref, masked, k_keep, pred, mpre)
     exact, excused = [], 0
     for b in seqs:
-        _characterise(res["dI"][b].astype(np.float64), masked[b], int(k_keep[b]),
+        _characterise(res["dI"][b].astype(np.float64), masked[b], int(k_gpu[b]),
                       pred, mpre, res["keep"][b], res["cand"][b])
+        if b in skip:
+            excused += 1
+            continue
         if (np.array_equal(res["keep"][b], keep_ref[b])
                 and np.array_equal(res["cand"][b], cand_ref[b])):
             exact.append(b)
@@ -271,3 +280,32 @@ def compare_constrained(inp: workloads.Inputs, res, masked, rules: int):
                          np.concatenate(want), TOL[kind]["out"], TIGHT[kind]["out"],
                          rel_scale=True)
     return exact
+
+
+def compare_dynamic(inp: workloads.Inputs, res, masked, yield_hist, alpha: float,
+                    rules: int):
+    """Dynamic budget: the GPU's K_b equals the oracle's reading except
+    where an oracle delta lies within GAP of the +Std threshold (the count
+    is then decided by rounding); the selection is then compared as in
+    compare_constrained with the oracle's K."""
+    cfg = inp.cfg
+    seqs = list(range(cfg.batch))
+    sub, sub_cu = sub_layers(inp.layers, inp.cu_prefix, cfg.block, seqs)
+    imps = [oracle.block_attn_importance(sub[l]["q"], sub[l]["k_blk"], sub[l]["v_blk"],
+                                         sub[l]["k_cache"], sub[l]["v_cache"], sub_cu,
+                                         cfg.block, cfg.hq, cfg.hkv)[1] for l in (0, 1)]
+    dI_ref = oracle.importance_delta(imps[0], imps[1], cfg.pool_k)
+    k_ref = oracle.dynamic_budget(dI_ref, masked, yield_hist, alpha)
+    k_gpu = res["k_used"]
+    skip = set()
+    for b in seqs:
+        if k_gpu[b] == k_ref[b]:
+            continue
+        v = dI_ref[b][np.asarray(masked[b]).astype(bool)]
+        margin = float(np.min(np.abs(v - (v.mean() + v.std()))))
+        assert margin < GAP, f"seq {b}: K gpu {k_gpu[b]} oracle {k_ref[b]} margin {margin}"
+        skip.add(b)
+    log(f"  dynamic budget: {cfg.batch - len(skip)} of {cfg.batch} K_b equal "
+        f"(K range {int(k_ref.min())}..{int(k_ref.max())})")
+    return compare_constrained(inp, res, masked, rules, k_keep=k_ref, k_gpu=k_gpu,
+                               skip=skip)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(F.lib, name), name
         assert callable(getattr(F, name)), name
@@ -198,6 +198,31 @@ def test_select_masked_rejects_bad_arguments(kw, code):
         a["masked"], a["k_keep"], a["rules"], a["keep"], a["cand"], a["dI"],
         a["idx"], a["cu_ret"], None) == code
     assert F.focus_last_error().startswith("focus_select_masked")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(B=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(pool_k=4), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(rules=8), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(alpha=0.0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(alpha=-1.0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), F.FOCUS_ERR_INVALID_ARG),
+    (dict(yield_hist=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(keep=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(idx=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(imp0=None), F.FOCUS_ERR_INVALID_ARG),
+])
+def test_select_dynamic_rejects_bad_arguments(kw, code):
+    a = dict(batch=2, B=32, Hq=32, pool_k=3, imp0=FAKE, imp1=FAKE, masked=None,
+             yield_hist=FAKE, alpha=1.5, rules=3, k_used=None, keep=FAKE,
+             cand=None, dI=None, idx=FAKE, cu_ret=FAKE)
+    a.update(kw)
+    assert F.lib.focus_select_dynamic(
+        a["batch"], a["B"], a["Hq"], a["pool_k"], a["imp0"], a["imp1"],
+        a["masked"], a["yield_hist"], a["alpha"], a["rules"], a["k_used"],
+        a["keep"], a["cand"], a["dI"], a["idx"], a["cu_ret"], None) == code
+    assert F.focus_last_error().startswith("focus_select_dynamic")
 
 
 def _ret(**kw):

@@ -356,3 +356,34 @@ def test_paged_prefix_equals_packed(name, over, plens, ps):
         assert torch.equal(imp, step.imp[li]) and torch.equal(lse, step.lse[li])
         if with_out:
             assert torch.equal(out, step.out[li])
+
+
+DYNAMIC = [
+    # overrides, prefix lengths, masked?, rules
+    (dict(), None, True, 3),
+    (dict(), None, False, 0),
+    (dict(block=128, pool_k=5), [100, 0, 2100, 64], True, 3),
+    (dict(block=7), [5, 90, 1, 0], True, 1),
+]
+
+
+@pytest.mark.parametrize("over,plens,use_mask,rules", DYNAMIC,
+                         ids=[f"B{d[0].get('block', 32)}-mask{int(d[2])}-rules{d[3]}"
+                              for d in DYNAMIC])
+def test_dynamic_budget_reading(over, plens, use_mask, rules):
+    """The dynamic budget (a labelled reading; parity against the pages is
+    unpinned) against the oracle's implementation of the same reading."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 32,
+                           **over)
+    log(f"[parity] dynamic budget B={cfg.block} N={cfg.batch} mask={use_mask} rules={rules}")
+    inp = workloads.make_inputs(cfg, 41, n_layers=3, prefix_lens=plens)
+    masked = (workloads.draw_masked(cfg, 41) if use_mask
+              else np.ones((cfg.batch, cfg.block), dtype=np.uint8))
+    y = workloads.draw_yield(cfg, 41)
+    step = FocusStep(parity.dims_of(cfg), inp.cu_prefix, inp.meta.k_keep,
+                     n_further=1, with_lse=True,
+                     masked=masked if use_mask else None, rules=rules,
+                     yield_hist=y, alpha=1.5)
+    step, res = parity.run_gpu(inp, step=step)
+    parity.compare_dynamic(inp, res, masked, y, 1.5, rules)

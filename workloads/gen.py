@@ -13,6 +13,7 @@ Recipe (per configuration, per seed):
   * per layer, Q / block K,V / prefix K,V are i.i.d. N(0, 1) float32 rounded
     to bf16 by round-to-nearest-even (float32 configs keep the float32
     values);
+  * decoding-yield history (for the dynamic budget): halves in [0, 6];
   * still-masked flags (for the masked-candidate selection): decoded
     fraction f_b ~ U[0, 0.75], position j decoded with probability
     clip(f_b * (1.5 - j / B), 0, 1);
@@ -103,6 +104,15 @@ def draw_masked(cfg: FocusConfig, seed: int = 0,
     p_dec = np.clip(f[:, None] * (1.5 - pos[None, :]), 0.0, 1.0)
     decoded = rng.random((n, blk)) < p_dec
     return (~decoded).astype(np.uint8)
+
+
+def draw_yield(cfg: FocusConfig, seed: int = 0) -> np.ndarray:
+    """Decoding-yield history per sequence for the dynamic budget: tokens
+    decoded at the previous step, drawn as halves in [0, 6] (exact in
+    float32) with mean near the pages' ~3 decoded tokens per step."""
+    rng = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([_ROOT, cfg.index, seed, 0x59494C44])))
+    return (rng.integers(0, 13, cfg.batch) / 2.0).astype(np.float32)
 
 
 def _randn(shape, cfg, seed, layer, name, device) -> torch.Tensor:
