@@ -33,14 +33,21 @@ namespace focus {
 namespace {
 
 constexpr int TK = 32;          // keys per tile
-constexpr int NSTAGE = 4;       // ring depth
+#ifndef FOCUS_RING_WO
+#define FOCUS_RING_WO 4
+#endif
+#ifndef FOCUS_RING_W8
+#define FOCUS_RING_W8 8
+#endif
+constexpr int NSTAGE = 4;       // ring depth (K-only ring; the smallest)
+// Ring depth: with O (K + V tiles, 16 KB a stage) and without (K only).
+template <bool WO> constexpr int ring_depth() { return WO ? FOCUS_RING_WO : NSTAGE; }
 constexpr int D = 128;
 constexpr int ROWB = D * 2;     // bytes per key row (256)
 constexpr int TILEB = TK * ROWB;        // 8 KB per K or V tile
 constexpr int PPITCH = TK + 4;          // fp32 probability row pitch
 // One ring stage holds a K tile and, when O is produced, a V tile.
 template <bool WO> constexpr int stage_bytes() { return WO ? 2 * TILEB : TILEB; }
-static_assert(kRowsPerWG * PPITCH * 4 <= NSTAGE * TILEB, "pass-2 buffer fits the ring");
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before O is rescaled
 constexpr int kPageRegs = 4;    // paged prefix: registers of cached page entries
@@ -61,19 +68,22 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 }
 
 // Wait until at most `n` of this wave's vector-memory operations are
-// outstanding (n in {0, 2, 4, 8}), then barrier. The memory clobber keeps
-// the compiler from moving LDS accesses across it.
+// outstanding, then barrier; n above 12 waits as for 12 (more than
+// needed, never less). The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+#define FOCUS_WB(N)                                                           \
+  case N:                                                                     \
+    asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    break;
 __device__ __forceinline__ void wait_and_barrier(int n) {
-  if (n >= 8) {
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else if (n >= 4) {
-    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else if (n >= 2) {
-    asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  switch (n < 0 ? 0 : (n > 12 ? 12 : n)) {
+    FOCUS_WB(0) FOCUS_WB(1) FOCUS_WB(2) FOCUS_WB(3) FOCUS_WB(4) FOCUS_WB(5)
+    FOCUS_WB(6) FOCUS_WB(7) FOCUS_WB(8) FOCUS_WB(9) FOCUS_WB(10) FOCUS_WB(11)
+    default:
+      FOCUS_WB(12)
   }
 }
+#undef FOCUS_WB
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
@@ -139,11 +149,19 @@ __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
 // NULL) no V is loaded and no P V product is formed; the K-only ring is half
 // the size and three workgroups share a CU.
 // PAGED: the prefix K/V live in pages (AttnArgs::page_table).
-template <bool RET, int NBT, bool WO, bool PAGED>
-__global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const AttnArgs a) {
+// NW: waves per workgroup, 4 (128 query rows) or 8 (256 rows, one
+// workgroup per CU with a deeper ring): with more than 128 rows per KV
+// head, 8 waves halve the number of workgroups that stream the same K/V.
+template <bool RET, int NBT, bool WO, bool PAGED, int NW>
+__global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
+    attn_bf16_kernel(const AttnArgs a) {
   constexpr int STAGEB = stage_bytes<WO>();
+  constexpr int NSTAGE = NW == 8 ? FOCUS_RING_W8 : ring_depth<WO>();
   constexpr int SMEM = NSTAGE * STAGEB;
-  constexpr int OPS = WO ? 4 : 2;  // loads per wave per tile
+  constexpr int NTHR = NW * 64;
+  constexpr int SPW = 8 / NW;                // 4-row DMA slots per wave
+  constexpr int OPS = (WO ? 2 : 1) * SPW;    // loads per wave per tile
+  static_assert(NW * 32 * PPITCH * 4 <= SMEM, "pass-2 buffer fits the ring");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -179,8 +197,8 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   const bool wave_on = wave * 32 < nh * a.rph;
 
   // ---- loader geometry: lane covers row (4j + lane/16) of DMA slot j,
-  // physical 16-byte chunk lane%16.
-  const int lrow0 = 8 * wave + (lane >> 4);   // rows lrow0 and lrow0 + 4
+  // physical 16-byte chunk lane%16; wave w owns slots SPW*w .. SPW*w+SPW-1.
+  const int lrow0 = 4 * SPW * wave + (lane >> 4);   // rows lrow0 + 4i
   const int pchunk = lane & 15;
   const int nbt = (nq + TK - 1) / TK;        // block tiles (<= NBT)
   const int npt = (plen + TK - 1) / TK;
@@ -189,12 +207,12 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   // Retained mode: the block rows this lane loads (gathered through idx),
   // resolved up front so that no index load sits between the streaming
   // loads. Block mode computes them from rbase.
-  int brow[RET ? NBT : 1][2];
+  int brow[RET ? NBT : 1][SPW];
   if constexpr (RET) {
 #pragma unroll
     for (int bt = 0; bt < NBT; ++bt) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < SPW; ++i) {
         // rows past the end repeat the last row (masked)
         const int j = min(bt * TK + lrow0 + 4 * i, nq - 1);
         brow[bt][i] = bt < nbt ? a.idx[rbase + j] : 0;
@@ -212,9 +230,9 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   // Byte offsets of the two rows this lane loads in a prefix tile, relative
   // to the tile's first token: full tiles add one scalar base per tile.
   // (32 rows of at most kMaxHeads heads stay below 2^32 bytes.)
-  uint32_t koff[2], voff[2];
+  uint32_t koff[SPW], voff[SPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < SPW; ++i) {
     const int lr = lrow0 + 4 * i;
     const uint32_t rb = (uint32_t)(lr * rowstride + goff);
     koff[i] = rb + ((pchunk ^ (lr & 15)) << 4);
@@ -284,8 +302,8 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
         // full prefix tile
         const size_t tb = (size_t)r0 * rowstride;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          char* dst = st + (2 * wave + i) * 1024;
+        for (int i = 0; i < SPW; ++i) {
+          char* dst = st + (SPW * wave + i) * 1024;
           dma16(kc + tb + koff[i], dst);
           if constexpr (WO) dma16(vc + tb + voff[i], dst + TILEB);
         }
@@ -293,12 +311,12 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
       }
       // last, partial prefix tile: rows past the end repeat the last row
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < SPW; ++i) {
         const int lr = lrow0 + 4 * i;          // row inside the tile
         const int64_t row = r0 + min(lr, plen - 1 - t * TK);
         // koff/voff hold lr * rowstride; take it back out in integers
         const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
-        char* dst = st + (2 * wave + i) * 1024;
+        char* dst = st + (SPW * wave + i) * 1024;
         dma16(kc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
         if constexpr (WO) dma16(vc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
       }
@@ -306,7 +324,7 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
     }
     const int bt = t - npt;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SPW; ++i) {
       const int lr = lrow0 + 4 * i;          // row inside the tile
       int row;
       if constexpr (RET) {
@@ -318,7 +336,7 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
         row = rbase + min(bt * TK + lr, nq - 1);
       }
       const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
-      char* dst = st + (2 * wave + i) * 1024;
+      char* dst = st + (SPW * wave + i) * 1024;
       dma16(kb + (size_t)((ptrdiff_t)koff[i] + shift), dst);
       if constexpr (WO) dma16(vb + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
     }
@@ -395,7 +413,8 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
   // the top; the ring slot of tile t - 1 is then refilled with tile t + 3.
   // cap, when given, receives the masked raw scores of a block tile.
   auto tile_step = [&](int t, f32x16& s_cur, f32x16& s_nxt, f32x16* cap) {
-    wait_and_barrier(t + 2 < nt ? OPS : 0);
+    // tiles t and t + 1 resident; t + 2 .. t + NSTAGE - 2 may be in flight
+    wait_and_barrier(OPS * max(0, min(t + NSTAGE - 2, nt - 1) - (t + 1)));
     if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
     if (!wave_on) return;
     if (t + 1 < nt) s_nxt = qk(t + 1);
@@ -528,7 +547,7 @@ __global__ void __launch_bounds__(kThreads, WO ? 2 : 3) attn_bf16_kernel(const A
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      for (int id = tid; id < nh * TK; id += kThreads) {
+      for (int id = tid; id < nh * TK; id += NTHR) {
         const int hh = id / TK;
         const int key = id - hh * TK;
         if (key < cnt) {
@@ -613,21 +632,30 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
     order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
 }
 
-template <bool RET, bool WO, bool PAGED>
-hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(kThreads);
+template <bool RET, bool WO, bool PAGED, int NW>
+hipError_t launch_nw(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(NW * 64);
   switch (nbt) {
     case 1:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED, NW>), grid, block, 0, s, a);
       break;
     case 2:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED, NW>), grid, block, 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED, NW>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
+}
+
+// Four waves (128 query rows) per workgroup. Eight-wave workgroups of 256
+// rows (one per CU, 8-stage ring), which halve the workgroups that stream
+// the same K/V when a KV head has more than 128 query rows, measured no
+// faster at B = 64 / 128 or G = 8, so they are not launched.
+template <bool RET, bool WO, bool PAGED>
+hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
+  return launch_nw<RET, WO, PAGED, kThreads / 64>(nbt, batch, a, s);
 }
 
 template <bool RET, bool WO>
