@@ -504,34 +504,16 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
   const float ltot = pair_sum(lsum);
   const float lse2 = mrun + log2f(ltot);
 
-  if (wave_on && row_ok) {
-    if constexpr (WO) {
-      const float inv = 1.0f / ltot;
-      __bf16* op = static_cast<__bf16*>(a.out) + ((size_t)(rbase + qi) * a.Hq + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * q4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * half) = o;
-        }
-      }
-    }
-    if constexpr (!RET) {
-      if (a.lse != nullptr && half == 0)
-        a.lse[((size_t)b * a.Hq + h) * a.B + qi] = lse2 * kLn2;
-    }
-  }
-
+  // The ring is idle from here on: the last tile waited for every load
+  // (vmcnt(0)), so the barriers below need no vmcnt wait, and the O stores
+  // come last, after the importance pass, so that nothing waits on them.
   if constexpr (!RET) {
     // Importance of the block columns: exp2(s*c - lse2) from the kept raw
     // block scores, summed down each column per head in a fixed order.
     float* pbuf = reinterpret_cast<float*>(smem);
     for (int bt = 0; bt < nbt; ++bt) {
       const int cnt = min(TK, nq - bt * TK);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (wave_on) {
         f32x16 sb = {};
 #pragma unroll
@@ -556,6 +538,49 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
           for (int i = 0; i < a.B; ++i) acc += col[i * PPITCH];
           const int hg = g * a.G + hc * a.hpw + hh;
           a.imp[((size_t)b * a.Hq + hg) * a.B + bt * TK + key] = acc;
+        }
+      }
+    }
+    if (wave_on && row_ok && a.lse != nullptr && half == 0)
+      a.lse[((size_t)b * a.Hq + h) * a.B + qi] = lse2 * kLn2;
+  }
+
+  if constexpr (WO) {
+    // O through LDS: each wave stages its 32 rows x 128 values (row pitch
+    // 272 bytes), then stores whole rows with 16-byte lanes, 4 rows of 256
+    // bytes per instruction. The staging area
+    // sits above the importance buffer; it overlaps the ring, so all waves
+    // must be past their last P V reads first.
+    constexpr int OP = 272;
+    if constexpr (RET) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(SMEM >= NW * 32 * OP + NW * 32 * PPITCH * 4, "O staging fits");
+    char* ost = smem + (SMEM - NW * 32 * OP) + wave * (32 * OP);
+    if (wave_on) {
+      const float inv = 1.0f / ltot;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * q4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(ost + n * OP + (dt * 32 + 8 * q4 + 4 * half) * 2) = o;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cidx = lane + 64 * k;           // 16-byte chunk of the wave's tile
+        const int row = cidx >> 4, c16 = cidx & 15;
+        const int rr = wave * 32 + row;
+        const int hl2 = rr / a.rph;
+        const int qi2 = rr - hl2 * a.rph;
+        if (hl2 < nh && qi2 < nq) {
+          const int h2 = g * a.G + hc * a.hpw + hl2;
+          const int qrow = rbase + qi2;           // output row (retained: its slot)
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.out) +
+                                    ((size_t)qrow * a.Hq + h2) * (D * 2) + c16 * 16) =
+              *reinterpret_cast<const u32x4*>(ost + row * OP + c16 * 16);
         }
       }
     }
