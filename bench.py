@@ -432,7 +432,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true>)",
+            "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false, 4>)",
             "algorithmic_bytes_per_launch": a_bytes,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
         },
