@@ -91,39 +91,41 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
 }
 
-// The eight V^T operand fragments of one 16-key step: for head-dim tiles
-// dt = 0..3 (addresses a0..a3) the keys at row offset +0 and +8 rows
-// (+2048 bytes), each read with ds_read_b64_tr_b16. The reads sit in one
-// asm block that also waits for them, so no output register is ever left
-// with a load in flight (and the compiler adds no wait of its own for the
+// The sixteen V^T operand fragments of one 32-key tile: for head-dim tiles
+// dt = 0..3 (addresses a0..a3) the keys at row offsets +0, +8 rows (f, the
+// first 16 keys) and +16, +24 rows (h, the last 16), each read with
+// ds_read_b64_tr_b16. The reads sit in one asm block that also waits for
+// them (one LDS wait per tile), so no output register is ever left with a
+// load in flight (and the compiler adds no wait of its own for the
 // direct-to-LDS loads that may still be landing in other ring stages). The
 // outputs are early-clobber: a read may land while a later read of the
 // block has not yet taken its address, so no output may share a register
 // with an address.
-#define FOCUS_TR8(OFF0, OFF1)                                                 \
-  asm volatile(                                                               \
-      "ds_read_b64_tr_b16 %0, %8 offset:" #OFF0 "\n\t"                        \
-      "ds_read_b64_tr_b16 %1, %8 offset:" #OFF1 "\n\t"                        \
-      "ds_read_b64_tr_b16 %2, %9 offset:" #OFF0 "\n\t"                        \
-      "ds_read_b64_tr_b16 %3, %9 offset:" #OFF1 "\n\t"                        \
-      "ds_read_b64_tr_b16 %4, %10 offset:" #OFF0 "\n\t"                       \
-      "ds_read_b64_tr_b16 %5, %10 offset:" #OFF1 "\n\t"                       \
-      "ds_read_b64_tr_b16 %6, %11 offset:" #OFF0 "\n\t"                       \
-      "ds_read_b64_tr_b16 %7, %11 offset:" #OFF1 "\n\t"                       \
-      "s_waitcnt lgkmcnt(0)"                                                  \
-      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]),      \
-        "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7])                                 \
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)                                    \
-      : "memory")
-
-template <int ST>
-__device__ __forceinline__ void v_frags(uint32_t a0, uint32_t a1, uint32_t a2,
-                                        uint32_t a3, u32x2v (&f)[8]) {
-  if constexpr (ST == 0) {
-    FOCUS_TR8(0, 2048);
-  } else {
-    FOCUS_TR8(4096, 6144);
-  }
+__device__ __forceinline__ void v_frags16(uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3, u32x2v (&f)[8], u32x2v (&h)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:0\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:0\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:0\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %12, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %13, %18 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+        "=&v"(f[6]), "=&v"(f[7]), "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]),
+        "=&v"(h[4]), "=&v"(h[5]), "=&v"(h[6]), "=&v"(h[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
 }
 
 // Max / sum of a value over the lane pair (l, l ^ 32), without LDS:
@@ -457,8 +459,8 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
 
     const uint32_t vbase = lds_addr(smem + (t % NSTAGE) * STAGEB + TILEB);
     u32x2v f0[8], f1[8];
-    v_frags<0>(vbase + va_off[0], vbase + va_off[1], vbase + va_off[2],
-               vbase + va_off[3], f0);
+    v_frags16(vbase + va_off[0], vbase + va_off[1], vbase + va_off[2],
+              vbase + va_off[3], f0, f1);
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[e]);
@@ -466,8 +468,6 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
     for (int dt = 0; dt < 4; ++dt)
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           cat8(f0[2 * dt], f0[2 * dt + 1]), pb, oacc[dt], 0, 0, 0);
-    v_frags<1>(vbase + va_off[0], vbase + va_off[1], vbase + va_off[2],
-               vbase + va_off[3], f1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 + e]);
 #pragma unroll
