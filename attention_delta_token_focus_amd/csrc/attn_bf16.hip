@@ -16,10 +16,15 @@
 //    serves 32 lanes of 8-byte reads per cycle; one such read touches 4 key
 //    rows x 64 bytes, so V's 16-byte chunks are XOR-swizzled by
 //    4 * (row mod 4), which spreads those 16 chunks over all banks.
-//  * Online softmax with the scale folded into one FMA per score and a
-//    lazy rescale of O: the running max only moves (and O is only rescaled)
-//    when a row max grows by more than 2^8; the final O / l and lse are
-//    exact whatever max was used.
+//  * Online softmax with the scale folded into one FMA per score. The
+//    exponentials of a tile are taken against the running max before the
+//    tile's own max is known; only when a lane's 16 of them sum to more
+//    than 2^8 (or are not finite, as on the first tile) is the max taken
+//    and O rescaled. The final O / l and lse are exact whatever max was
+//    used, and no exponential exceeds 2^8.
+//  * Inside one wave the matrix core and the vector ALU overlap: the eight
+//    score MFMAs of tile t + 1 are issued one at a time between the
+//    exponentials of tile t (scheduling fences keep that order).
 //  * The block keys are processed last and their raw scores stay in
 //    registers, so the importance pass needs neither a reload nor a
 //    recompute once the final lse is known (and those registers are free
@@ -49,7 +54,9 @@ constexpr int PPITCH = TK + 4;          // fp32 probability row pitch
 // One ring stage holds a K tile and, when O is produced, a V tile.
 template <bool WO> constexpr int stage_bytes() { return WO ? 2 * TILEB : TILEB; }
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;   // log2 headroom before O is rescaled
+// A lane's sum of the 16 exponentials of a tile above which the running
+// max is recomputed (and O rescaled).
+constexpr float kSumMax = 256.0f;
 constexpr int kPageRegs = 4;    // paged prefix: registers of cached page entries
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their
 // maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -140,6 +147,14 @@ __device__ __forceinline__ float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                   false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of a lane's 16 exponentials, pairwise in a fixed order.
+__device__ __forceinline__ float tile_sum(const f32x16& p) {
+  float q8[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) q8[v] = p[2 * v] + p[2 * v + 1];
+  return ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
 }
 
 __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
@@ -414,12 +429,11 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
   // of tile t (s_cur) and its P V product. Tiles t and t + 1 are resident at
   // the top; the ring slot of tile t - 1 is then refilled with tile t + 3.
   // cap, when given, receives the masked raw scores of a block tile.
-  auto tile_step = [&](int t, f32x16& s_cur, f32x16& s_nxt, f32x16* cap) {
+  auto tile_step = [&](int t, f32x16& s_cur, f32x16& s_nxt, f32x16* cap, bool more) {
     // tiles t and t + 1 resident; t + 2 .. t + NSTAGE - 2 may be in flight
     wait_and_barrier(OPS * max(0, min(t + NSTAGE - 2, nt - 1) - (t + 1)));
     if (t + NSTAGE - 1 < nt) issue_tile(t + NSTAGE - 1);
     if (!wave_on) return;
-    if (t + 1 < nt) s_nxt = qk(t + 1);
 
     f32x16& s = s_cur;
     const int cnt = tile_cnt(t);
@@ -431,15 +445,49 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
       }
     }
     if (cap != nullptr) *cap = s;
-    const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
-    const float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
-    const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
-    const float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
-    const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
-    const float mm = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
-    const float mx = pair_max(mm) * c;
-    if (__any(mx > mrun + kLazy)) {
-      const float mnew = fmaxf(mrun, mx);
+    // Exponentials against the running max first; the max of this tile is
+    // only needed when their sum exceeds kSumMax or is not finite (the
+    // first tile: mrun = -inf). They are interleaved with the score MFMAs
+    // of tile t + 1 (more: a tile follows), so that the vector ALU and the
+    // matrix core of this wave work at the same time; the fences keep the
+    // compiler from regrouping them.
+    f32x16 p;
+    float q8[8];
+    if (more) {
+      const char* ks = smem + ((t + 1) % NSTAGE) * STAGEB;
+      bf16x8 kf[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int ch = (2 * k + half) ^ (n & 15);
+        kf[k] = *reinterpret_cast<const bf16x8*>(ks + krd + ch * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 acc = {};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], acc, 0, 0, 0);
+        p[2 * k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], c, -mrun));
+        p[2 * k + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], c, -mrun));
+        q8[k] = p[2 * k] + p[2 * k + 1];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_nxt = acc;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q8[k] = p[2 * k] + p[2 * k + 1];
+    }
+    float ts = ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
+    if (__any(!(ts <= kSumMax))) {
+      const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
+      const float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+      const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
+      const float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+      const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+      const float mm = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
+      const float mnew = fmaxf(mrun, pair_max(mm) * c);
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       mrun = mnew;
       lsum *= alpha;
@@ -447,14 +495,13 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
       }
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
+      ts = tile_sum(p);
     }
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
-    float q8[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) q8[v] = s[2 * v] + s[2 * v + 1];
-    lsum += ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
+    lsum += ts;
+    s = p;
     if constexpr (!WO) return;
 
     const uint32_t vbase = lds_addr(smem + (t % NSTAGE) * STAGEB + TILEB);
@@ -484,9 +531,11 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
   // instead of being copied between iterations; then the block tiles,
   // unrolled, each keeping its raw scores in registers of its own for the
   // importance pass (live only from here on).
+  // (A wave with rows has nq >= 1, hence a block tile after every prefix
+  // tile.)
   for (int t = 0; t < npt; t += 2) {
-    tile_step(t, sa, sb, nullptr);
-    if (t + 1 < npt) tile_step(t + 1, sb, sa, nullptr);
+    tile_step(t, sa, sb, nullptr, true);
+    if (t + 1 < npt) tile_step(t + 1, sb, sa, nullptr, true);
   }
   if (npt & 1) sa = sb;
 #pragma unroll
@@ -495,9 +544,9 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
       f32x16* cap = nullptr;
       if constexpr (!RET) cap = &sblk[bt];
       if (bt & 1)
-        tile_step(npt + bt, sb, sa, cap);
+        tile_step(npt + bt, sb, sa, cap, npt + bt + 1 < nt);
       else
-        tile_step(npt + bt, sa, sb, cap);
+        tile_step(npt + bt, sa, sb, cap, npt + bt + 1 < nt);
     }
   }
 

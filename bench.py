@@ -297,6 +297,29 @@ def time_masked_select(cfg, inp, dims, n_further, args):
     }
 
 
+def stream_read_reference(args, gib=4):
+    """Read bandwidth of a plain device reduction (torch row sums of a
+    4 GiB float32 matrix of 8192 rows, one pass; the fastest torch read
+    measured on this GPU), timed like the attention launches: the measured
+    stream-read figure the block attention is also compared with."""
+    x = torch.ones((8192, (gib << 30) // 4 // 8192), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum(dim=1)
+    stream = torch.cuda.current_stream()
+    n = max(3, min(10, args.steps))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        x.sum(dim=1)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    del x
+    return {"kernel": f"torch row sums of a {gib} GiB float32 matrix (8192 rows)",
+            "GBs": round((gib << 30) / (us / 1e6) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,7 +425,9 @@ def main() -> int:
             "dynamic_budget_reading": time_dynamic_select(cfg, inp, dims, args),
         }
 
+    stream_ref = stream_read_reference(args)
     traffic = load_traffic(cfg.name)
+    attn_us = np.asarray(attn_ms) * 1e3
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -435,6 +460,10 @@ def main() -> int:
             "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false, 4>)",
             "algorithmic_bytes_per_launch": a_bytes,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
+            "launch_us_p10_p50_p90": [round(float(np.percentile(attn_us, q)), 2)
+                                      for q in (10, 50, 90)],
+            "stream_read_reference": dict(
+                stream_ref, attn_frac_of_it=round(achieved / stream_ref["GBs"], 4)),
         },
         "breakdown_us": {
             "schedule": round(float(np.mean(sched_ms)) * 1e3, 2),
