@@ -5,8 +5,10 @@
 // sources on the pages); this file only changes how the work is mapped on
 // the chip:
 //  * K/V tiles of 32 keys travel HBM -> LDS by direct-to-LDS loads
-//    (global_load_lds_dwordx4) through a ring of 4 stages, so three tiles
-//    are in flight while one is computed and no registers hold loads.
+//    (buffer_load_dwordx4 ... lds for whole prefix tiles, addressed from a
+//    scalar per-tile base; global_load_lds_dwordx4 for the rest) through a
+//    ring of 4 stages, so three tiles are in flight while one is computed
+//    and no registers hold loads.
 //    Completion is tracked by hand: each wave waits until its own loads for
 //    the tile are done (vmcnt), then one barrier per tile publishes them.
 //  * K rows sit in LDS with their 16-byte chunks XOR-swizzled by the row
@@ -69,6 +71,23 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // the non-temporal cache policy (nt), which measured 6% faster for the
 // retained-query launch and neutral for the block launch.
 constexpr int kStreamPolicy = 2;  // cache-policy bits: nt
+
+// A wave-uniform pointer, moved to scalar registers explicitly.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer resource at a tile's first byte (gfx9 word 3: 32-bit data
+// format, no swizzle); lane offsets stay far below its 2 GiB range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, kStreamPolicy);
+}
 
 __device__ __forceinline__ void dma16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, kStreamPolicy);
@@ -182,7 +201,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int lane = tid & 63;
   const int n = lane & 31;
   const int half = lane >> 5;
@@ -318,11 +337,22 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
       if ((t + 1) * TK <= plen) {
         // full prefix tile
         const size_t tb = (size_t)r0 * rowstride;
+        // A full tile is addressed as a buffer at the tile's first byte (the
+        // 64-bit base in scalar registers) plus the lane's constant 32-bit
+        // offset: no vector address arithmetic per load.
+        const auto rk = tile_rsrc(uniform_ptr(kc + tb));
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           char* dst = st + (SPW * wave + i) * 1024;
-          dma16(kc + tb + koff[i], dst);
-          if constexpr (WO) dma16(vc + tb + voff[i], dst + TILEB);
+          dma16b(rk, koff[i], dst);
+        }
+        if constexpr (WO) {
+          const auto rv = tile_rsrc(uniform_ptr(vc + tb));
+#pragma unroll
+          for (int i = 0; i < SPW; ++i) {
+            char* dst = st + (SPW * wave + i) * 1024;
+            dma16b(rv, voff[i], dst + TILEB);
+          }
         }
         return;
       }
