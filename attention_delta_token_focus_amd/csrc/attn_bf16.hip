@@ -40,15 +40,10 @@ namespace focus {
 namespace {
 
 constexpr int TK = 32;          // keys per tile
-#ifndef FOCUS_RING_WO
-#define FOCUS_RING_WO 4
-#endif
-#ifndef FOCUS_RING_W8
-#define FOCUS_RING_W8 8
-#endif
-constexpr int NSTAGE = 4;       // ring depth (K-only ring; the smallest)
-// Ring depth: with O (K + V tiles, 16 KB a stage) and without (K only).
-template <bool WO> constexpr int ring_depth() { return WO ? FOCUS_RING_WO : NSTAGE; }
+// Ring depth, with O (K + V tiles, 16 KB a stage) and without (K only):
+// four stages measured best for both (three to five were tried).
+constexpr int NSTAGE = 4;
+constexpr int NW = kThreads / 64;  // waves per workgroup (128 query rows)
 constexpr int D = 128;
 constexpr int ROWB = D * 2;     // bytes per key row (256)
 constexpr int TILEB = TK * ROWB;        // 8 KB per K or V tile
@@ -185,14 +180,14 @@ __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
 // NULL) no V is loaded and no P V product is formed; the K-only ring is half
 // the size and three workgroups share a CU.
 // PAGED: the prefix K/V live in pages (AttnArgs::page_table).
-// NW: waves per workgroup, 4 (128 query rows) or 8 (256 rows, one
-// workgroup per CU with a deeper ring): with more than 128 rows per KV
-// head, 8 waves halve the number of workgroups that stream the same K/V.
-template <bool RET, int NBT, bool WO, bool PAGED, int NW>
-__global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : (WO ? 2 : 3))
+// Four waves per workgroup (NW); eight-wave workgroups of 256 rows (one per
+// CU, 8-stage ring), which halve the workgroups that stream the same K/V
+// when a KV head has more than 128 query rows, measured no faster at
+// B = 64 / 128 or G = 8.
+template <bool RET, int NBT, bool WO, bool PAGED>
+__global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
     attn_bf16_kernel(const AttnArgs a) {
   constexpr int STAGEB = stage_bytes<WO>();
-  constexpr int NSTAGE = NW == 8 ? FOCUS_RING_W8 : ring_depth<WO>();
   constexpr int SMEM = NSTAGE * STAGEB;
   constexpr int NTHR = NW * 64;
   constexpr int SPW = 8 / NW;                // 4-row DMA slots per wave
@@ -738,30 +733,21 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
     order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
 }
 
-template <bool RET, bool WO, bool PAGED, int NW>
-hipError_t launch_nw(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
+template <bool RET, bool WO, bool PAGED>
+hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(NW * 64);
   switch (nbt) {
     case 1:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED, NW>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED>), grid, block, 0, s, a);
       break;
     case 2:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED, NW>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED>), grid, block, 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED, NW>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
-}
-
-// Four waves (128 query rows) per workgroup. Eight-wave workgroups of 256
-// rows (one per CU, 8-stage ring), which halve the workgroups that stream
-// the same K/V when a KV head has more than 128 query rows, measured no
-// faster at B = 64 / 128 or G = 8, so they are not launched.
-template <bool RET, bool WO, bool PAGED>
-hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
-  return launch_nw<RET, WO, PAGED, kThreads / 64>(nbt, batch, a, s);
 }
 
 template <bool RET, bool WO>

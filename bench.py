@@ -457,7 +457,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false, 4>)",
+            "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false>)",
             "algorithmic_bytes_per_launch": a_bytes,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
             "launch_us_p10_p50_p90": [round(float(np.percentile(attn_us, q)), 2)
