@@ -36,6 +36,7 @@ import workloads  # noqa: E402
 METRIC = ("block-steps/sec at B=32, batch 256 (importance+evict); "
           "% of HBM peak BW")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of an MI355X
 ATTN_SRC = os.path.join(ROOT, "attention_delta_token_focus_amd", "csrc",
                         "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_attn_c3.json")
@@ -53,6 +54,14 @@ def attn_bytes(cfg, prefix_lens, with_lse=False, with_out=True) -> int:
     if with_lse:
         per_seq += 4 * hq * blk
     return int(n * per_seq + f * int(prefix_lens.sum()) * hkv * d * e)
+
+
+def attn_flops(cfg, prefix_lens) -> int:
+    """Algorithmic flops of one block-attention launch: Q K^T and P V over
+    the P_b prefix keys and the B block keys, 2 flops per multiply-add:
+    4 * Hq * B * (P_b + B) * d per sequence."""
+    blk, hq, d = cfg.block, cfg.hq, cfg.head_dim
+    return int(4 * hq * blk * d * (prefix_lens.astype(np.int64) + blk).sum())
 
 
 def select_bytes(cfg, n_ret) -> int:
@@ -406,6 +415,10 @@ def main() -> int:
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     a_bytes = attn_bytes(cfg, plen)
     achieved = a_bytes / attn_avg_s / 1e9
+    # The launch is bound by whichever roof is lower: HBM below the ridge of
+    # MFMA_BF16_PEAK / HBM_PEAK flops per byte, the matrix cores above it.
+    a_flops = attn_flops(cfg, plen)
+    mfma_bound = a_flops / a_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     ms_per_step = total_ms / args.steps
     value = cfg.batch * args.steps / (total_ms / 1e3)
     n_ret = step.n_ret
@@ -453,10 +466,16 @@ def main() -> int:
             "further_layers": n_further, "seed": args.seed,
         },
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(a_flops / attn_avg_s / 1e12, 1) if mfma_bound else round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round((a_flops / attn_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS) if mfma_bound
+                          else achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "hbm_GBs": round(achieved, 1),
+            "flops_per_launch": a_flops,
+            "flops_per_byte": round(a_flops / a_bytes, 1),
             "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false>)",
             "algorithmic_bytes_per_launch": a_bytes,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
