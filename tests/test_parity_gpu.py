@@ -194,6 +194,18 @@ def test_c5_full_size_sampled():
     _full_size("c5", "c5", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 64])
 
 
+def test_c4_full_size_sampled():
+    """B = 128 (four block tiles, four workgroups per KV head), fixed
+    2048-token prefixes: first, middle and last sequence."""
+    _full_size("c4", "c4", lambda p: [0, 31, 63])
+
+
+def test_c6_full_size_sampled():
+    """B = 64 (two block tiles, two workgroups per KV head), lognormal
+    prefixes: longest, shortest and two fixed sequences."""
+    _full_size("c6", "c6", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 0, 100])
+
+
 @pytest.mark.parametrize("over,plens,kk", [
     (dict(), None, None),
     (dict(block=128, pool_k=5), [100, 0, 2100], [32, 0, 128]),
