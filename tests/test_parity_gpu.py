@@ -66,6 +66,10 @@ EDGE = [
     ("bf16 d64 G8 B32", dict(head_dim=64, hq=16, hkv=2), [100, 300], [11, 6]),
     ("B16 G8 two chunks", dict(block=16, hq=16, hkv=1), [33, 17], [4, 16]),
     ("B33 G4", dict(block=33, hq=8, hkv=2), [31, 200], [10, 33]),
+    # prefixes past 4096 tokens beside short ones
+    ("long B32", dict(block=32, hq=8, hkv=2), [5000, 4200, 33, 1], [5, 32, 1, 0]),
+    ("long B128", dict(block=128, hq=8, hkv=2, pool_k=5), [4500, 0], [32, 128]),
+    ("long B48 G8", dict(block=48, hq=16, hkv=2), [4100, 4097, 95], [9, 48, 3]),
 ]
 
 
@@ -87,6 +91,21 @@ def test_retained_with_full_budget_equals_block_attention():
     step, res = parity.run_gpu(inp, layers_dev=lay)
     assert step.n_ret == 5 * 32
     assert np.array_equal(res["idx"], np.arange(160))
+    got, ref = res["ret"][0], res["out"][1]
+    err = float(np.abs(got - ref).max())
+    log(f"  retained vs block max abs diff {err:.3e}")
+    assert err <= 1e-6
+
+
+def test_retained_with_full_budget_equals_block_attention_long():
+    """The same cross-call pin with prefixes past 4096 tokens."""
+    cfg = workloads.scaled(workloads.get("c3"), batch=3, hq=8, hkv=2)
+    log("[parity] cross pin retained == block attention, long prefixes")
+    inp = workloads.make_inputs(cfg, 4, n_layers=2, prefix_lens=[5000, 33, 4097],
+                                k_keep=[32] * 3)
+    lay = parity.to_device(inp)
+    lay = [lay[0], lay[1], lay[1]]
+    step, res = parity.run_gpu(inp, layers_dev=lay)
     got, ref = res["ret"][0], res["out"][1]
     err = float(np.abs(got - ref).max())
     log(f"  retained vs block max abs diff {err:.3e}")
@@ -212,6 +231,7 @@ def test_c6_full_size_sampled():
     (dict(block=7), [5, 90, 1, 0], [0, 7, 3, 1]),
     (dict(block=48, hq=16, hkv=2), [40, 333], [9, 48]),
     (dict(dtype="f32", head_dim=64, hq=4, hkv=1), [70, 3], [8, 32]),
+    (dict(hq=8, hkv=2), [5000, 300], [8, 32]),
 ])
 def test_layer1_importance_only(over, plens, kk):
     """out=NULL on layer 1 (no V read, no P V): the oracle still matches
@@ -321,6 +341,7 @@ PAGED = [
     ("B128 pages of 128", dict(block=128, pool_k=5), [100, 0, 2100], 128),
     ("B7 ragged pages of 96", dict(block=7), [5, 90, 1, 0, 200], 96),
     ("f32 d64 pages of 64", dict(dtype="f32", head_dim=64, hq=4, hkv=1), [70, 3, 130], 64),
+    ("long prefixes pages of 64", dict(hq=8, hkv=2), [5000, 4097, 64], 64),
 ]
 
 
