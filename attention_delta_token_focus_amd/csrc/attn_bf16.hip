@@ -7,8 +7,8 @@
 //  * K/V tiles of 32 keys travel HBM -> LDS by direct-to-LDS loads
 //    (buffer_load_dwordx4 ... lds for whole prefix tiles, addressed from a
 //    scalar per-tile base; global_load_lds_dwordx4 for the rest) through a
-//    ring of 4 stages, so three tiles are in flight while one is computed
-//    and no registers hold loads.
+//    ring of 4 stages: while tile t is computed, tile t + 1 is resident
+//    and tiles t + 2 and t + 3 are in flight; no registers hold loads.
 //    Completion is tracked by hand: each wave waits until its own loads for
 //    the tile are done (vmcnt), then one barrier per tile publishes them.
 //  * K rows sit in LDS with their 16-byte chunks XOR-swizzled by the row
@@ -32,8 +32,8 @@
 //    recompute once the final lse is known (and those registers are free
 //    during the prefix stream).
 //  * Work items are visited longest prefix first (order from a one-block
-//    bitonic sort of the prefix lengths), the 8 KV heads of a sequence on
-//    neighbouring workgroups.
+//    rank count, or bitonic sort past 256 sequences, of the prefix
+//    lengths), the KV heads of a sequence on neighbouring workgroups.
 #include "focus_internal.hpp"
 
 namespace focus {
