@@ -10,10 +10,10 @@ One step = one pass of the whole hot path over one batch:
 Inputs are seeded synthetic tensors made on the device before timing.
 
 Prints one JSON line. `value` is block-steps/s (sequences through the step
-per second). `roofline` is for the dominant kernel (block attention +
-importance), timed with HIP events around each of its launches inside the
-timed region. `cpu_baseline` times the float64 oracle on a bounded sample of
-the same workload on the host cores.
+per second) over K steps run back to back. `roofline` is for the dominant
+kernel (block attention + importance), timed with HIP events around each
+of its launches in a second pass of K steps. `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -78,20 +78,28 @@ def retained_bytes(cfg, prefix_lens, n_ret) -> int:
                + 2 * int(prefix_lens.sum()) * hkv * d * e)
 
 
-def source_sha(path) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_sha(path) -> str:
+    """Hash of a source file's code: // comments, trailing blanks and empty
+    lines removed, so that a comment edit keeps a measurement taken on the
+    same code, and any code change invalidates it."""
+    lines = []
+    with open(path) as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def load_traffic(cfg_name):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, only
-    if it was taken on the current kernel source."""
+    if it was taken on the current kernel code."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != source_sha(ATTN_SRC) or \
+    if t.get("kernel_code_sha") != code_sha(ATTN_SRC) or \
             t.get("workload") != cfg_name:
         return None
     return t.get("hbm_bytes_per_launch")
@@ -155,12 +163,17 @@ def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
     for _ in range(max(1, args.warmup // 2)):
         step.run(layers)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-          for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    for s in range(args.steps):
+        step.run(layers)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(args.steps)]
     for s in range(args.steps):
         step.schedule()
         step.block_attn(layers[0], 0)
@@ -170,9 +183,7 @@ def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
         step.select()
         for i, lay in enumerate(layers[2:2 + n_further]):
             step.retained(lay, i)
-    t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
     l1_s = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
     b = attn_bytes(cfg, plen, with_out=False)
     return {
