@@ -84,7 +84,8 @@ hipError_t launch_retained_attn(Elem e, int d, int batch, const AttnArgs& a,
 // Tuned bf16 / head_dim 128 kernels (attn_bf16.hip).
 hipError_t launch_block_attn_bf16(int batch, const AttnArgs& a, hipStream_t s);
 hipError_t launch_retained_attn_bf16(int batch, const AttnArgs& a, hipStream_t s);
-// Longest-prefix-first order of the sequences into `order` [batch].
+// Longest-prefix-first order of the sequences into `order` [batch]
+// (schedule.hip).
 hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
                             hipStream_t s);
 size_t order_workspace_bytes(int batch);

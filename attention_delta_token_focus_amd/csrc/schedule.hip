@@ -1,0 +1,99 @@
+// Visiting order of the sequences for one step's attention calls: the
+// longest prefix first. The attention work of a sequence grows with its
+// prefix length; handing the longest ones out first keeps every compute
+// unit busy until the end of a launch (longest-processing-time-first
+// list scheduling).
+#include "focus_internal.hpp"
+
+namespace focus {
+namespace {
+
+// Longest-prefix-first visiting order of the sequences; equal lengths keep
+// the lower sequence first. Up to 256 sequences: one 256-thread block,
+// thread i counts the sequences that go before sequence i (lengths
+// broadcast from LDS, four per read) and writes i at that rank. Up to
+// kMaxSort: bitonic sort of (P_b, ~b) in LDS by 1024 threads. Larger
+// batches keep their natural order.
+constexpr int kMaxSort = 8192;
+constexpr int kRankMax = 256;
+
+__global__ void __launch_bounds__(256) lpt_rank_kernel(
+    int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
+  __shared__ __attribute__((aligned(16))) int len[kRankMax];
+  const int tid = threadIdx.x;
+  const int n4 = (batch + 3) & ~3;
+  int mine = -1;
+  if (tid < batch) mine = cu_prefix[tid + 1] - cu_prefix[tid];
+  if (tid < n4) len[tid] = mine;
+  __syncthreads();
+  if (tid < batch) {
+    int rank = 0;
+    // unrolled so that several LDS reads are in flight, not one at a time
+#pragma unroll 8
+    for (int j = 0; j < n4; j += 4) {
+      const int4 l4 = *reinterpret_cast<const int4*>(len + j);
+      rank += (l4.x > mine) + (l4.x == mine && j < tid);
+      rank += (l4.y > mine) + (l4.y == mine && j + 1 < tid);
+      rank += (l4.z > mine) + (l4.z == mine && j + 2 < tid);
+      rank += (l4.w > mine) + (l4.w == mine && j + 3 < tid);
+    }
+    order[rank] = tid;
+  }
+}
+
+__global__ void __launch_bounds__(1024) lpt_sort_kernel(
+    int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kMaxSort];
+  const int tid = threadIdx.x;
+  if (batch > kMaxSort) {
+    for (int i = tid; i < batch; i += 1024) order[i] = i;
+    return;
+  }
+  int n2 = 1;
+  while (n2 < batch) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) {
+    uint64_t k = 0;
+    if (i < batch) {
+      const uint32_t len = (uint32_t)(cu_prefix[i + 1] - cu_prefix[i]);
+      k = ((uint64_t)len << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += 1024) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t x = key[i], y = key[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? x < y : x > y) {
+            key[i] = y;
+            key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < batch; i += 1024)
+    order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
+}
+
+}  // namespace
+
+size_t order_workspace_bytes(int batch) {
+  return ((size_t)batch * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
+                            hipStream_t s) {
+  if (batch <= kRankMax) {
+    hipLaunchKernelGGL(lpt_rank_kernel, dim3(1), dim3(256), 0, s, batch, cu_prefix, order);
+  } else {
+    hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace focus
