@@ -112,6 +112,27 @@ def test_retained_with_full_budget_equals_block_attention_long():
     assert err <= 1e-6
 
 
+@pytest.mark.parametrize("batch", [1, 7, 256, 257, 1000, 8192, 8193])
+def test_schedule_order(batch):
+    """focus_schedule: longest prefix first, equal lengths by lower index
+    (a stable sort on the negated lengths), on both sides of the 256-sequence
+    rank kernel / bitonic sort switch and of the 8192 limit past which the
+    natural order is kept. Lengths repeat often, to exercise the ties."""
+    import attention_delta_token_focus_amd as F
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(0, 40, size=batch) * 32 + rng.integers(0, 2, size=batch)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    order = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    F.focus_schedule(batch, cu, order)
+    torch.cuda.synchronize()
+    got = order.cpu().numpy()
+    if batch > 8192:
+        want = np.arange(batch)
+    else:
+        want = np.argsort(-lens, kind="stable")
+    assert np.array_equal(got, want)
+
+
 def test_visiting_order_does_not_change_results():
     """With order=NULL (the call schedules itself), with focus_schedule's
     order, and with the reversed order, every output is bitwise equal."""
