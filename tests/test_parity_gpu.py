@@ -66,6 +66,9 @@ EDGE = [
     ("bf16 d64 G8 B32", dict(head_dim=64, hq=16, hkv=2), [100, 300], [11, 6]),
     ("B16 G8 two chunks", dict(block=16, hq=16, hkv=1), [33, 17], [4, 16]),
     ("B33 G4", dict(block=33, hq=8, hkv=2), [31, 200], [10, 33]),
+    ("G1 bf16 d128", dict(hq=8, hkv=8), [100, 2000, 0], [5, 32, 3]),
+    ("G2 bf16 d128", dict(hq=8, hkv=4), [33, 700], [12, 1]),
+    ("G16 B8 one workgroup", dict(block=8, hq=32, hkv=2, pool_k=3), [64, 257, 5], [2, 8, 4]),
     # prefixes past 4096 tokens beside short ones
     ("long B32", dict(block=32, hq=8, hkv=2), [5000, 4200, 33, 1], [5, 32, 1, 0]),
     ("long B128", dict(block=128, hq=8, hkv=2, pool_k=5), [4500, 0], [32, 128]),
