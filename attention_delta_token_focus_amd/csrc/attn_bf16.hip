@@ -19,11 +19,13 @@
 //    rows x 64 bytes, so V's 16-byte chunks are XOR-swizzled by
 //    4 * (row mod 4), which spreads those 16 chunks over all banks.
 //  * Online softmax with the scale folded into one FMA per score. The
-//    exponentials of a tile are taken against the running max before the
-//    tile's own max is known; only when a lane's 16 of them sum to more
-//    than 2^8 (or are not finite, as on the first tile) is the max taken
-//    and O rescaled. The final O / l and lse are exact whatever max was
-//    used, and no exponential exceeds 2^8.
+//    running max starts at the first tile's max; the exponentials of a
+//    later tile are taken against it before the tile's own max is known,
+//    in place of the raw scores. Only when a lane's 16 of them sum to more
+//    than 2^8 (or are not finite) is the max taken, from raw scores
+//    recomputed out of the still-resident K tile, and O rescaled. The final
+//    O / l and lse are exact whatever max was used, and no exponential
+//    exceeds 2^8.
 //  * Inside one wave the matrix core and the vector ALU overlap: the eight
 //    score MFMAs of tile t + 1 are issued one at a time between the
 //    exponentials of tile t (scheduling fences keep that order).
@@ -442,6 +444,26 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   auto tile_cnt = [&](int t) {
     return t < npt ? min(TK, plen - t * TK) : min(TK, nq - (t - npt) * TK);
   };
+  // Keys past the tile's count get score -inf.
+  auto mask_tile = [&](f32x16& s, int cnt) {
+    if (cnt < TK) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 8 * (v >> 2) + 4 * half + (v & 3);
+        if (key >= cnt) s[v] = -INFINITY;
+      }
+    }
+  };
+  // Max of a row's scores in the log2 domain (both lanes of the row).
+  auto row_max2 = [&](const f32x16& s) {
+    const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    const float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
+    const float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float mm = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
+    return pair_max(mm) * c;
+  };
 
   // V^T fragment offsets inside a V tile, one per head-dim tile.
   uint32_t va_off[4];
@@ -462,21 +484,14 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
 
     f32x16& s = s_cur;
     const int cnt = tile_cnt(t);
-    if (cnt < TK) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = 8 * (v >> 2) + 4 * half + (v & 3);
-        if (key >= cnt) s[v] = -INFINITY;
-      }
-    }
+    mask_tile(s, cnt);
     if (cap != nullptr) *cap = s;
-    // Exponentials against the running max first; the max of this tile is
-    // only needed when their sum exceeds kSumMax or is not finite (the
-    // first tile: mrun = -inf). They are interleaved with the score MFMAs
+    // Exponentials against the running max first, in place of the raw
+    // scores; the max of this tile is only needed when their sum exceeds
+    // kSumMax or is not finite. They are interleaved with the score MFMAs
     // of tile t + 1 (more: a tile follows), so that the vector ALU and the
     // matrix core of this wave work at the same time; the fences keep the
     // compiler from regrouping them.
-    f32x16 p;
     float q8[8];
     if (more) {
       const char* ks = smem + ((t + 1) % NSTAGE) * STAGEB;
@@ -491,28 +506,32 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], acc, 0, 0, 0);
-        p[2 * k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], c, -mrun));
-        p[2 * k + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], c, -mrun));
-        q8[k] = p[2 * k] + p[2 * k + 1];
+        s[2 * k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], c, -mrun));
+        s[2 * k + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], c, -mrun));
+        q8[k] = s[2 * k] + s[2 * k + 1];
         __builtin_amdgcn_sched_barrier(0);
       }
       s_nxt = acc;
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
+        s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) q8[k] = p[2 * k] + p[2 * k + 1];
+      for (int k = 0; k < 8; ++k) q8[k] = s[2 * k] + s[2 * k + 1];
     }
     float ts = ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
     if (__any(!(ts <= kSumMax))) {
-      const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
-      const float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
-      const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
-      const float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
-      const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
-      const float mm = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
-      const float mnew = fmaxf(mrun, pair_max(mm) * c);
+      // The raw scores were overwritten: a block tile kept them (cap);
+      // otherwise tile t is still resident in the ring and they are
+      // recomputed (the same MFMA chain, the same bits).
+      f32x16 r;
+      if (cap != nullptr) {
+        r = *cap;
+      } else {
+        r = qk(t);
+        mask_tile(r, cnt);
+      }
+      const float mnew = fmaxf(mrun, row_max2(r));
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       mrun = mnew;
       lsum *= alpha;
@@ -522,11 +541,10 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mrun));
-      ts = tile_sum(p);
+        s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(r[v], c, -mrun));
+      ts = tile_sum(s);
     }
     lsum += ts;
-    s = p;
     if constexpr (!WO) return;
 
     const uint32_t vbase = lds_addr(smem + (t % NSTAGE) * STAGEB + TILEB);
@@ -551,7 +569,13 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   // Tile 0 must be in LDS before its scores; tiles 1.. may still land.
   wait_and_barrier(OPS * (min(nt, NSTAGE - 1) - 1));
   f32x16 sa = {}, sb = {};
-  if (wave_on) sa = qk(0);
+  if (wave_on) {
+    // The running max starts at the first tile's max, so that tile takes
+    // the common path (same values as rescaling from -inf).
+    sa = qk(0);
+    mask_tile(sa, tile_cnt(0));
+    mrun = row_max2(sa);
+  }
   // Prefix tiles two at a time, so that the score registers alternate
   // instead of being copied between iterations; then the block tiles,
   // unrolled, each keeping its raw scores in registers of its own for the
