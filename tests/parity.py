@@ -140,10 +140,17 @@ def assert_close(name, got, ref, tol, tight=None, rel_scale=False):
 
 
 def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=None,
-                 further_check: bool = True) -> SelectionReport:
-    """Oracle block-step on sequences `seqs` against the GPU results."""
+                 further_check: bool = True, bar_scale: float = 1.0) -> SelectionReport:
+    """Oracle block-step on sequences `seqs` against the GPU results.
+
+    bar_scale multiplies the bars of lse, importance and delta: with scores
+    far from O(1) their rounding error grows with the magnitude (one fp32
+    ulp of an exponent argument s is |s| * 2^-23); O is a normalised mix
+    and keeps its bars."""
     cfg = inp.cfg
     blk, kind = cfg.block, cfg.dtype
+    tol = {k: v * (bar_scale if k != "out" else 1.0) for k, v in TOL[kind].items()}
+    tight = {k: v * (bar_scale if k != "out" else 1.0) for k, v in TIGHT[kind].items()}
     seqs = list(seqs)
     layers = layers_host if layers_host is not None else inp.layers
     sub, sub_cu = sub_layers(layers, inp.cu_prefix, blk, seqs)
@@ -154,13 +161,13 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
     for l in (0, 1):
         if res["out"][l] is not None:   # None: importance-only call
             assert_close(f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
-                         TOL[kind]["out"], TIGHT[kind]["out"], rel_scale=True)
-        assert_close(f"imp L{l}", res["imp"][l][seqs], o[l][1], TOL[kind]["imp"],
-                     TIGHT[kind]["imp"])
+                         tol["out"], tight["out"], rel_scale=True)
+        assert_close(f"imp L{l}", res["imp"][l][seqs], o[l][1], tol["imp"],
+                     tight["imp"])
         if res["lse"][l] is not None:
-            assert_close(f"lse L{l}", res["lse"][l][seqs], o[l][2], TIGHT[kind]["lse"])
+            assert_close(f"lse L{l}", res["lse"][l][seqs], o[l][2], tight["lse"])
     dI_ref = oracle.importance_delta(o[0][1], o[1][1], cfg.pool_k)
-    assert_close("dI", res["dI"][seqs], dI_ref, TIGHT[kind]["dI"])
+    assert_close("dI", res["dI"][seqs], dI_ref, tight["dI"])
 
     # The GPU's selection is a valid top-K of the GPU's own delta: every
     # kept position beats every evicted one, equal deltas by lower index.
@@ -209,8 +216,8 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
                 continue
             got = np.concatenate([ret[g_cu[seqs[i]]:g_cu[seqs[i] + 1]] for i in exact])
             want = np.concatenate([ref[cu_ref[i]:cu_ref[i + 1]] for i in exact])
-            assert_close(f"retained L{2 + li}", got, want, TOL[kind]["out"],
-                         TIGHT[kind]["out"], rel_scale=True)
+            assert_close(f"retained L{2 + li}", got, want, tol["out"],
+                         tight["out"], rel_scale=True)
     return rep
 
 

@@ -115,6 +115,95 @@ def test_retained_with_full_budget_equals_block_attention_long():
     assert err <= 1e-6
 
 
+HOT = [
+    # name, overrides, prefix lengths, hot keys (layer, tensor, seq, pos, scale)
+    ("bf16 d128 G4", dict(hq=8, hkv=2), [300, 97, 1000, 40], [
+        (0, "k_cache", 0, 100, 1.3),    # full prefix tile 3, sum above 2^8
+        (0, "k_cache", 1, 96, 13.0),    # last, one-key prefix tile, overflow
+        (0, "k_blk", 2, 5, 13.0),       # block key (kept raw scores)
+        (0, "k_cache", 3, 3, 13.0),     # first tile: sets the running max
+        (1, "k_cache", 2, 700, 1.3),
+        (1, "k_blk", 3, 20, 1.3),
+        (2, "k_cache", 0, 250, 13.0),   # retained attention, prefix tile
+        (2, "k_blk", 1, 10, 1.3),       # retained attention, gathered keys
+        (2, "k_blk", 3, 31, 13.0),
+    ]),
+    ("bf16 B128 G4", dict(block=128, hq=8, hkv=2, pool_k=5), [130, 0], [
+        (0, "k_cache", 0, 129, 13.0),
+        (0, "k_blk", 0, 100, 1.3),
+        (0, "k_blk", 1, 70, 13.0),
+        (2, "k_blk", 1, 127, 1.3),
+        (2, "k_cache", 0, 40, 1.3),
+    ]),
+    ("f32 d64 G4", dict(dtype="f32", head_dim=64, hq=4, hkv=1), [200, 65], [
+        (0, "k_cache", 0, 150, 1.3),
+        (0, "k_cache", 1, 64, 13.0),
+        (0, "k_blk", 1, 2, 13.0),
+        (2, "k_cache", 1, 33, 13.0),
+    ]),
+]
+
+
+@pytest.mark.parametrize("name,over,plens,hot", HOT, ids=[h[0] for h in HOT])
+def test_rescale_path_hot_keys(name, over, plens, hot):
+    """Keys planted as a scaled copy of one query of their group make that
+    query's score jump far above the running max after the first tile
+    (scale 1.3: about 15 above, the tile's exponential sum passes 2^8;
+    scale 13: about 150 above, the exponentials overflow), so the kernels'
+    rescale path runs on prefix, block and retained tiles, packed and
+    paged, with and without O. Every token is kept, so retained attention
+    is compared on every sequence."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c2"), batch=len(plens), prefix_fixed=1,
+                           **over)
+    log(f"[parity] hot keys {name}: N={cfg.batch} B={cfg.block} {cfg.dtype} "
+        f"d={cfg.head_dim}")
+    inp = workloads.make_inputs(cfg, 21, n_layers=3, prefix_lens=plens,
+                                k_keep=[cfg.block] * cfg.batch)
+    cu = np.asarray(inp.cu_prefix, dtype=np.int64)
+    blk, G = cfg.block, cfg.hq // cfg.hkv
+    smax = 0.0
+    for li, where, b, pos, scale in hot:
+        L = inp.layers[li]
+        g = cfg.hkv - 1                       # the last KV group
+        qv = L["q"][b * blk + pos % blk, g * G].float()
+        row = int(cu[b]) + pos if where == "k_cache" else b * blk + pos
+        assert (where == "k_blk" and pos < blk) or pos < cu[b + 1] - cu[b]
+        L[where][row, g] = (scale * qv).to(L[where].dtype)
+        smax = max(smax, float(qv @ L[where][row, g].float()) / cfg.head_dim ** 0.5)
+    lay = parity.to_device(inp)
+    step, res = parity.run_gpu(inp, layers_dev=lay)
+    # fp32 bars (1e-5) are about one ulp of an exponent argument near 94;
+    # they grow with the planted magnitude. The bf16 bars are ten times
+    # wider and hold as they are.
+    scale = max(1.0, smax / 8.0) if cfg.dtype == "f32" else 1.0
+    parity.compare_step(inp, res, range(cfg.batch), bar_scale=scale)
+    # Layer 0 again: importance only, and paged prefix (bf16 kernels), both
+    # bitwise equal to the packed call with O.
+    dm = step.dims
+    L = lay[0]
+    imp = torch.empty_like(step.imp[0])
+    lse = torch.empty_like(step.lse[0])
+    F.focus_block_attn_importance(
+        F.dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv, dm.head_dim, 0.0,
+        L["q"], L["k_blk"], None, L["k_cache"], None, step.cu_prefix, step.order,
+        step.max_prefix, None, imp, lse, step.ws, step.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(imp, step.imp[0]) and torch.equal(lse, step.lse[0])
+    if cfg.dtype == "bf16":
+        kp, table, pps = _paged_pool(L["k_cache"], cu, 64, 7)
+        vp, _, _ = _paged_pool(L["v_cache"], cu, 64, 7)
+        out = torch.empty_like(step.out[0])
+        F.focus_block_attn_importance_paged(
+            F.dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv, dm.head_dim,
+            0.0, L["q"], L["k_blk"], L["v_blk"], kp, vp, table, 64, pps,
+            step.cu_prefix, step.order, step.max_prefix, out, imp, lse, step.ws,
+            step.ws_bytes)
+        torch.cuda.synchronize()
+        assert torch.equal(out, step.out[0])
+        assert torch.equal(imp, step.imp[0]) and torch.equal(lse, step.lse[0])
+
+
 @pytest.mark.parametrize("batch", [1, 7, 256, 257, 1000, 8192, 8193])
 def test_schedule_order(batch):
     """focus_schedule: longest prefix first, equal lengths by lower index
