@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   constexpr int NTHR = NW * 64;
   constexpr int SPW = 8 / NW;                // 4-row DMA slots per wave
   constexpr int OPS = (WO ? 2 : 1) * SPW;    // loads per wave per tile
-  static_assert(NW * 32 * PPITCH * 4 <= SMEM, "pass-2 buffer fits the ring");
+  static_assert(NW * 32 * PPITCH * 4 + NTHR * 4 <= SMEM, "pass-2 buffers fit the ring");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -609,8 +609,17 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   // come last, after the importance pass, so that nothing waits on them.
   if constexpr (!RET) {
     // Importance of the block columns: exp2(s*c - lse2) from the kept raw
-    // block scores, summed down each column per head in a fixed order.
+    // block scores, summed down each column per head in a fixed order: with
+    // fewer than NTHR (head, key) columns, every thread adds a segment of
+    // rows of one column and one thread per column then adds the segments
+    // in order (a column of B = 128 rows is 8 segments of 16, not one
+    // chain of 128 LDS reads); otherwise each column has at most 16 rows
+    // and one thread adds it.
     float* pbuf = reinterpret_cast<float*>(smem);
+    float* part = pbuf + NW * 32 * PPITCH;           // segment sums, <= NTHR
+    const int ncol = nh * TK;
+    const int nseg = max(1, NTHR / ncol);
+    const int seg = (a.B + nseg - 1) / nseg;
     for (int bt = 0; bt < nbt; ++bt) {
       const int cnt = min(TK, nq - bt * TK);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -629,13 +638,39 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      for (int id = tid; id < nh * TK; id += NTHR) {
-        const int hh = id / TK;
-        const int key = id - hh * TK;
+      if (nseg == 1) {
+        for (int cl = tid; cl < ncol; cl += NTHR) {
+          const int hh = cl / TK;
+          const int key = cl - hh * TK;
+          if (key < cnt) {
+            float acc = 0.f;
+            const float* col = pbuf + (hh * a.rph) * PPITCH + key;
+            for (int i = 0; i < a.B; ++i) acc += col[i * PPITCH];
+            const int hg = g * a.G + hc * a.hpw + hh;
+            a.imp[((size_t)b * a.Hq + hg) * a.B + bt * TK + key] = acc;
+          }
+        }
+        continue;
+      }
+      if (tid < ncol * nseg) {
+        const int sg = tid / ncol;
+        const int cl = tid - sg * ncol;
+        const int hh = cl / TK;
+        const int key = cl - hh * TK;
+        const int i1 = min(a.B, (sg + 1) * seg);
+        const float* col = pbuf + (hh * a.rph) * PPITCH + key;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int i = sg * seg; i < i1; ++i) acc += col[i * PPITCH];
+        part[tid] = acc;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tid < ncol) {
+        const int hh = tid / TK;
+        const int key = tid - hh * TK;
         if (key < cnt) {
           float acc = 0.f;
-          const float* col = pbuf + (hh * a.rph) * PPITCH + key;
-          for (int i = 0; i < a.B; ++i) acc += col[i * PPITCH];
+          for (int sg = 0; sg < nseg; ++sg) acc += part[sg * ncol + tid];
           const int hg = g * a.G + hc * a.hpw + hh;
           a.imp[((size_t)b * a.Hq + hg) * a.B + bt * TK + key] = acc;
         }
@@ -653,7 +688,7 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
     // must be past their last P V reads first.
     constexpr int OP = 272;
     if constexpr (RET) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    static_assert(SMEM >= NW * 32 * OP + NW * 32 * PPITCH * 4, "O staging fits");
+    static_assert(SMEM >= NW * 32 * OP + NW * 32 * PPITCH * 4 + NTHR * 4, "O staging fits");
     char* ost = smem + (SMEM - NW * 32 * OP) + wave * (32 * OP);
     if (wave_on) {
       const float inv = 1.0f / ltot;
