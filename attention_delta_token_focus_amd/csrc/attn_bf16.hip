@@ -213,7 +213,11 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   const int b = a.order != nullptr ? min(max(a.order[rank], 0), a.batch - 1) : rank;
 
   const int p0 = a.cu_prefix[b];
-  const int plen = a.cu_prefix[b + 1] - p0;
+  // Paged prefix: a length past the sequence's page-table row (a broken
+  // max_prefix promise) is cut there, so no entry of another row is read.
+  const int plen = PAGED
+      ? min(a.cu_prefix[b + 1] - p0, a.pages_per_seq * a.page_size)
+      : a.cu_prefix[b + 1] - p0;
   int rbase, nq;
   if constexpr (RET) {
     rbase = a.cu_ret[b];

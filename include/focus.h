@@ -151,7 +151,10 @@ focus_status focus_block_attn_importance(
  *              Entries past a sequence's last page are not read.
  *  page_size   tokens per page, a positive multiple of 32.
  *  pages_per_seq  row stride of page_table; pages_per_seq * page_size
- *              must cover max_prefix.
+ *              must cover max_prefix. A sequence whose cu_prefix length
+ *              exceeds pages_per_seq * page_size (a broken max_prefix
+ *              promise) is cut at the end of its row: only the tokens its
+ *              row holds are attended, and no other row is read.
  *  cu_prefix   as above; only the lengths cu_prefix[b+1] - cu_prefix[b]
  *              are used.
  * Other arguments as focus_block_attn_importance.

@@ -504,6 +504,53 @@ def test_paged_prefix_equals_packed(name, over, plens, ps):
             assert torch.equal(out, step.out[li])
 
 
+def test_paged_prefix_longer_than_its_row_is_cut():
+    """A cu_prefix length past pages_per_seq * page_size (a broken
+    max_prefix promise) is cut at the end of the sequence's page-table row:
+    the result is bitwise the packed call on the cut prefix, for the tuned
+    bf16 kernel and the generic fp32 one."""
+    import attention_delta_token_focus_amd as F
+    for over in (dict(hq=8, hkv=2), dict(dtype="f32", head_dim=64, hq=4, hkv=1)):
+        cfg = workloads.scaled(workloads.get("c3"), batch=3, prefix_fixed=1, **over)
+        ps, pps = 64, 2                              # rows hold 128 tokens
+        claimed, cut = [200, 100, 129], [128, 100, 128]
+        log(f"[parity] paged prefix cut at its row: {cfg.dtype} d={cfg.head_dim}")
+        inp = workloads.make_inputs(cfg, 51, n_layers=2, prefix_lens=claimed)
+        L = parity.to_device(inp)[0]
+        cu_long = np.concatenate([[0], np.cumsum(claimed)]).astype(np.int32)
+        cu_cut = np.concatenate([[0], np.cumsum(cut)]).astype(np.int32)
+        keep_rows = np.concatenate([np.arange(cu_long[b], cu_long[b] + cut[b])
+                                    for b in range(cfg.batch)])
+        rows = torch.as_tensor(keep_rows, device="cuda")
+        kc, vc = L["k_cache"][rows].contiguous(), L["v_cache"][rows].contiguous()
+        kp, table, got_pps = _paged_pool(kc, cu_cut, ps, 9)
+        vp, _, _ = _paged_pool(vc, cu_cut, ps, 9)
+        assert got_pps == pps
+        dt = F.dtype_code(workloads.torch_dtype(cfg))
+        n, blk, hq, hkv, d = cfg.batch, cfg.block, cfg.hq, cfg.hkv, cfg.head_dim
+        ws_bytes = F.focus_block_attn_importance_workspace(n, blk, hq, hkv, d, ps * pps)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        outs = []
+        for paged in (True, False):
+            out = torch.empty_like(L["q"])
+            imp = torch.empty((n, hq, blk), dtype=torch.float32, device="cuda")
+            lse = torch.empty_like(imp)
+            if paged:
+                F.focus_block_attn_importance_paged(
+                    dt, n, blk, hq, hkv, d, 0.0, L["q"], L["k_blk"], L["v_blk"], kp, vp,
+                    table, ps, pps, torch.as_tensor(cu_long, device="cuda"), None,
+                    ps * pps, out, imp, lse, ws, ws_bytes)
+            else:
+                F.focus_block_attn_importance(
+                    dt, n, blk, hq, hkv, d, 0.0, L["q"], L["k_blk"], L["v_blk"], kc, vc,
+                    torch.as_tensor(cu_cut, device="cuda"), None, max(cut), out, imp,
+                    lse, ws, ws_bytes)
+            torch.cuda.synchronize()
+            outs.append((out, imp, lse))
+        for x, y in zip(*outs):
+            assert torch.equal(x, y)
+
+
 DYNAMIC = [
     # overrides, prefix lengths, masked?, rules
     (dict(), None, True, 3),
