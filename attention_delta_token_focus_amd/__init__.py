@@ -18,12 +18,15 @@ import torch
 __all__ = [
     "FOCUS_OK", "FOCUS_ERR_INVALID_ARG", "FOCUS_ERR_UNSUPPORTED",
     "FOCUS_ERR_WORKSPACE", "FOCUS_ERR_HIP", "FOCUS_F32", "FOCUS_BF16",
+    "FOCUS_KEEP_PREDECESSOR", "FOCUS_KEEP_MASKED_PREFIX",
     "FocusError", "lib", "lib_path", "dtype_code", "focus_version",
-    "focus_status_string", "focus_last_error",
+    "focus_status_string", "focus_last_error", "focus_schedule",
     "focus_block_attn_importance_workspace", "focus_block_attn_importance",
-    "focus_delta_topk", "focus_compact", "focus_select", "focus_schedule",
-    "focus_retained_attn_workspace",
-    "focus_retained_attn",
+    "focus_block_attn_importance_paged",
+    "focus_delta_topk", "focus_compact", "focus_select", "focus_select_masked",
+    "focus_select_dynamic",
+    "focus_retained_attn_workspace", "focus_retained_attn",
+    "focus_retained_attn_paged",
 ]
 
 FOCUS_OK = 0
