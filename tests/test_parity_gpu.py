@@ -69,6 +69,9 @@ EDGE = [
     ("G1 bf16 d128", dict(hq=8, hkv=8), [100, 2000, 0], [5, 32, 3]),
     ("G2 bf16 d128", dict(hq=8, hkv=4), [33, 700], [12, 1]),
     ("G16 B8 one workgroup", dict(block=8, hq=32, hkv=2, pool_k=3), [64, 257, 5], [2, 8, 4]),
+    ("B96 three block tiles", dict(block=96, hq=8, hkv=2, pool_k=5), [300, 0, 97], [24, 96, 1]),
+    ("B65 one-key block tile", dict(block=65, hq=8, hkv=2), [64, 129], [65, 13]),
+    ("G32 eight head chunks", dict(hq=64, hkv=2), [200, 31], [8, 32]),
     # prefixes past 4096 tokens beside short ones
     ("long B32", dict(block=32, hq=8, hkv=2), [5000, 4200, 33, 1], [5, 32, 1, 0]),
     ("long B128", dict(block=128, hq=8, hkv=2, pool_k=5), [4500, 0], [32, 128]),
