@@ -340,6 +340,16 @@ def stream_read_reference(args, gib=4):
             "GBs": round((gib << 30) / (us / 1e6) / 1e9, 1)}
 
 
+def attn_kernel_name(cfg) -> str:
+    """The block-attention kernel instantiation the workload runs: the
+    tuned bf16 d = 128 kernel with 1, 2 or 4 block tiles of 32 keys, else
+    the generic kernel."""
+    if cfg.dtype != "bf16" or cfg.head_dim != 128:
+        return "attn_kernel (generic)"
+    nbt = 1 if cfg.block <= 32 else (2 if cfg.block <= 64 else 4)
+    return f"attn_bf16_kernel<false, {nbt}, true, false>"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -506,7 +516,7 @@ def main() -> int:
             "hbm_GBs": round(achieved, 1),
             "flops_per_launch": a_flops,
             "flops_per_byte": round(a_flops / a_bytes, 1),
-            "kernel": "block attention + importance (attn_bf16_kernel<false, 1, true, false>)",
+            "kernel": "block attention + importance (%s)" % attn_kernel_name(cfg),
             "algorithmic_bytes_per_launch": a_bytes,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
             "launch_us_p10_p50_p90": [round(float(np.percentile(attn_us, q)), 2)
