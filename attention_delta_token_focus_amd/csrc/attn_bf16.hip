@@ -32,7 +32,8 @@
 //  * The block keys are processed last and their raw scores stay in
 //    registers, so the importance pass needs neither a reload nor a
 //    recompute once the final lse is known (and those registers are free
-//    during the prefix stream).
+//    during the prefix stream). Its column sums run in two fixed-order
+//    levels over all threads (row segments, then the segments in order).
 //  * Work items are visited longest prefix first (order from a one-block
 //    rank count, or bitonic sort past 256 sequences, of the prefix
 //    lengths), the KV heads of a sequence on neighbouring workgroups.
