@@ -9,36 +9,42 @@ namespace focus {
 namespace {
 
 // Longest-prefix-first visiting order of the sequences; equal lengths keep
-// the lower sequence first. Up to 256 sequences: one 256-thread block,
-// thread i counts the sequences that go before sequence i (lengths
-// broadcast from LDS, four per read) and writes i at that rank. Up to
-// kMaxSort: bitonic sort of (P_b, ~b) in LDS by 1024 threads. Larger
-// batches keep their natural order.
+// the lower sequence first. Up to 256 sequences: one 1024-thread block;
+// the four threads i, i + 256, i + 512, i + 768 each count, over a quarter
+// of the lengths (broadcast from LDS, four per read), the sequences that go
+// before sequence i; the four counts add up to its rank. Up to kMaxSort:
+// bitonic sort of (P_b, ~b) in LDS by 1024 threads. Larger batches keep
+// their natural order.
 constexpr int kMaxSort = 8192;
 constexpr int kRankMax = 256;
 
-__global__ void __launch_bounds__(256) lpt_rank_kernel(
+__global__ void __launch_bounds__(1024) lpt_rank_kernel(
     int batch, const int32_t* __restrict__ cu_prefix, int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(16))) int len[kRankMax];
+  __shared__ int part[4][kRankMax];
   const int tid = threadIdx.x;
+  const int i = tid & (kRankMax - 1);       // the sequence ranked
+  const int q = tid >> 8;                   // the quarter of the lengths
   const int n4 = (batch + 3) & ~3;
-  int mine = -1;
-  if (tid < batch) mine = cu_prefix[tid + 1] - cu_prefix[tid];
-  if (tid < n4) len[tid] = mine;
+  if (tid < n4) len[tid] = tid < batch ? cu_prefix[tid + 1] - cu_prefix[tid] : -1;
   __syncthreads();
-  if (tid < batch) {
-    int rank = 0;
+  int rank = 0;
+  if (i < batch) {
+    const int mine = len[i];
+    const int j1 = min(n4, 64 * (q + 1));
     // unrolled so that several LDS reads are in flight, not one at a time
-#pragma unroll 8
-    for (int j = 0; j < n4; j += 4) {
+#pragma unroll 4
+    for (int j = 64 * q; j < j1; j += 4) {
       const int4 l4 = *reinterpret_cast<const int4*>(len + j);
-      rank += (l4.x > mine) + (l4.x == mine && j < tid);
-      rank += (l4.y > mine) + (l4.y == mine && j + 1 < tid);
-      rank += (l4.z > mine) + (l4.z == mine && j + 2 < tid);
-      rank += (l4.w > mine) + (l4.w == mine && j + 3 < tid);
+      rank += (l4.x > mine) + (l4.x == mine && j < i);
+      rank += (l4.y > mine) + (l4.y == mine && j + 1 < i);
+      rank += (l4.z > mine) + (l4.z == mine && j + 2 < i);
+      rank += (l4.w > mine) + (l4.w == mine && j + 3 < i);
     }
-    order[rank] = tid;
   }
+  part[q][i] = rank;
+  __syncthreads();
+  if (tid < batch) order[part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]] = tid;
 }
 
 __global__ void __launch_bounds__(1024) lpt_sort_kernel(
@@ -89,7 +95,7 @@ size_t order_workspace_bytes(int batch) {
 hipError_t launch_lpt_order(int batch, const int32_t* cu_prefix, int32_t* order,
                             hipStream_t s) {
   if (batch <= kRankMax) {
-    hipLaunchKernelGGL(lpt_rank_kernel, dim3(1), dim3(256), 0, s, batch, cu_prefix, order);
+    hipLaunchKernelGGL(lpt_rank_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
   } else {
     hipLaunchKernelGGL(lpt_sort_kernel, dim3(1), dim3(1024), 0, s, batch, cu_prefix, order);
   }
