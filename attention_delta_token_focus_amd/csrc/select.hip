@@ -297,14 +297,17 @@ __global__ void __launch_bounds__(64) select_kernel(
 
 // One workgroup of 1024 threads walks the batch in chunks of 1024
 // sequences. Thread t owns sequence base + t: it counts its kept bytes
-// (16-byte loads when rows are 16-byte aligned), the workgroup takes an
-// exclusive scan of the counts (wavefront shuffles + LDS), and the thread
-// writes its sequence's kept indices in ascending order.
+// (16-byte loads when rows are 16-byte aligned) and the workgroup takes an
+// exclusive scan of the counts (wavefront shuffles + LDS). Then each
+// wavefront writes the kept indices of one sequence at a time, lane j for
+// position j (its rank among the kept positions from a ballot), so that the
+// indices of a sequence leave in one contiguous store, ascending.
 template <bool VEC>
 __global__ void __launch_bounds__(1024) compact_kernel(
     int batch, int B, const uint8_t* __restrict__ keep,
     int32_t* __restrict__ idx, int32_t* __restrict__ cu_ret) {
   __shared__ int wsum[16];
+  __shared__ int offs[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -312,11 +315,11 @@ __global__ void __launch_bounds__(1024) compact_kernel(
   for (int base = 0; base < batch; base += 1024) {
     const int b = base + tid;
     const bool live = b < batch;
-    u32x4 row[8];  // up to 128 keep bytes
     int cnt = 0;
     if constexpr (VEC) {
       const int nv = B >> 4;
       const u32x4* kp = reinterpret_cast<const u32x4*>(keep + (size_t)b * B);
+      u32x4 row[8];  // up to 128 keep bytes
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         row[v] = (live && v < nv) ? kp[v] : u32x4{0, 0, 0, 0};
@@ -355,26 +358,24 @@ __global__ void __launch_bounds__(1024) compact_kernel(
       if (lane < 16) wsum[lane] = w;
     }
     __syncthreads();
-    int off = carry + (wave ? wsum[wave - 1] : 0) + x - cnt;
+    const int off = carry + (wave ? wsum[wave - 1] : 0) + x - cnt;
     const int chunk_total = wsum[15];
-    if (live) {
-      cu_ret[b] = off;
-      if constexpr (VEC) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = 16 * v + 4 * w + e;
-              if (j < B && ((row[v][w] >> (8 * e)) & 0xFFu) != 0) idx[off++] = b * B + j;
-            }
-          }
-        }
-      } else {
-        const uint8_t* kp = keep + (size_t)b * B;
-        for (int j = 0; j < B; ++j)
-          if (kp[j] != 0) idx[off++] = b * B + j;
+    offs[tid] = off;
+    if (live) cu_ret[b] = off;
+    __syncthreads();
+    const int nseq = min(1024, batch - base);
+    for (int s = wave; s < nseq; s += 16) {
+      const int bs = base + s;
+      const uint8_t* kp = keep + (size_t)bs * B;
+      int o = offs[s];
+      for (int j0 = 0; j0 < B; j0 += 64) {
+        const int j = j0 + lane;
+        const bool k = j < B && kp[j] != 0;
+        const uint64_t m = __ballot(k);
+        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (k) idx[o + r] = bs * B + j;
+        o += __popcll(m);
       }
     }
     carry += chunk_total;
