@@ -21,6 +21,7 @@ PINS = [
     lambda: P.test_golden_block_attention_importance("scale_d4.json"),
     P.test_golden_delta_topk_compact,
     P.test_golden_retained,
+    P.test_golden_block_step,
     lambda: P.test_column_sums_equal_block_size(7, 4, 2, 16, [0, 5, 13]),
     P.test_zero_queries_closed_form,
     P.test_dominant_key_takes_all_weight,
@@ -108,6 +109,27 @@ MUTANTS = [
         "vals = [float(d_imp[b, j]) for j in range(blk)]", 0)]),
     ("budget: no floor of one", [("k[b] = min(len(vals), max(1, want))",
                                   "k[b] = min(len(vals), want)", 0)]),
+    ("step: layers 0 and 1 swapped", [(
+        'for name, lay in (("l0", layer0), ("l1", layer1)):',
+        'for name, lay in (("l0", layer1), ("l1", layer0)):', 0)]),
+    ("step: delta arguments swapped", [(
+        'importance_delta(res["imp_l0"], res["imp_l1"], pool_k)',
+        'importance_delta(res["imp_l1"], res["imp_l0"], pool_k)', 0)]),
+    ("step: pool size ignored", [(
+        'importance_delta(res["imp_l0"], res["imp_l1"], pool_k)',
+        'importance_delta(res["imp_l0"], res["imp_l1"], 1)', 0)]),
+    ("step: k_keep replaced by B", [(
+        'res["keep"] = topk_keep(res["dI"], k_keep)',
+        'res["keep"] = topk_keep(res["dI"], [block] * len(k_keep))', 0)]),
+    ("step: further layer i reads layer i+1", [(
+        "for lay in further_layers]",
+        "for lay in list(further_layers[1:]) + list(further_layers[:1])]", 0)]),
+    ("step: further layers read layer 1's block tensors", [(
+        'retained_attn(lay["q"], lay["k_blk"], lay["v_blk"], res["idx"],',
+        'retained_attn(lay["q"], layer1["k_blk"], layer1["v_blk"], res["idx"],', 0)]),
+    ("step: further layers read layer 0's prefix cache", [(
+        'res["cu_ret"], lay["k_cache"], lay["v_cache"],',
+        'res["cu_ret"], layer0["k_cache"], layer0["v_cache"],', 0)]),
 ]
 
 EXPORTED = ["attention_rows", "block_attn_importance", "block_step", "compact",

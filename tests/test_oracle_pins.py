@@ -53,6 +53,48 @@ def test_golden_block_attention_importance(name):
             atol=1e-14)
 
 
+def _golden_block_step_layers(g):
+    """The layer dicts of tests/golden/block_step_tiny.json (d = 1)."""
+    n = len(g["cu_prefix"]) - 1
+    rows = n * g["block"]
+    qh = golden_io.arr(g["q_heads"])
+    q = np.broadcast_to(qh[None, :, None], (rows, g["hq"], 1)).copy()
+
+    def lay(name):
+        L = g["layers"][name]
+        d = {k: golden_io.arr(L[k]).reshape(-1, g["hkv"], 1)
+             for k in ("k_blk", "v_blk", "k_cache", "v_cache")}
+        d["q"] = q
+        return d
+    return [lay(name) for name in ("l0", "l1", "fA", "fB")]
+
+
+def test_golden_block_step():
+    """The whole step, worked by hand (layer order of the delta, budgets,
+    compaction, and which layer each further retained attention reads)."""
+    g = golden_io.load("block_step_tiny.json")
+    blk, hq = g["block"], g["hq"]
+    l0, l1, fa, fb = _golden_block_step_layers(g)
+    res = oracle.block_step(l0, l1, g["cu_prefix"], g["k_keep"], blk, hq,
+                            g["hkv"], g["pool_k"], further_layers=[fa, fb])
+    e = g["expect"]
+    for name in ("out_l0", "out_l1"):
+        per_seq = golden_io.arr(e[name])                  # [N, Hq]
+        want = np.repeat(per_seq, blk, axis=0)[:, :, None]
+        np.testing.assert_allclose(res[name], want, atol=1e-13)
+    for name in ("lse_l0", "lse_l1"):
+        want = np.repeat(golden_io.arr(e[name])[:, :, None], blk, axis=2)
+        np.testing.assert_allclose(res[name], want, atol=1e-13)
+    for name in ("imp_l0", "imp_l1", "dI"):
+        np.testing.assert_allclose(res[name], golden_io.arr(e[name]), atol=1e-13)
+    np.testing.assert_array_equal(res["keep"], np.array(e["keep"]))
+    np.testing.assert_array_equal(res["idx"], e["idx"])
+    np.testing.assert_array_equal(res["cu_ret"], e["cu_ret"])
+    assert len(res["retained_out"]) == 2
+    for got, want in zip(res["retained_out"], e["retained_out"]):
+        np.testing.assert_allclose(got, golden_io.arr(want)[:, :, None], atol=1e-12)
+
+
 def test_golden_delta_topk_compact():
     g = golden_io.load("delta_topk_compact.json")
     imp0, imp1 = golden_io.arr(g["imp0"]), golden_io.arr(g["imp1"])
@@ -217,6 +259,21 @@ def test_maxpool_matches_torch(k):
     np.testing.assert_array_equal(got, ref.numpy())
     if k == 1:
         np.testing.assert_array_equal(got, imp.mean(axis=1))
+
+
+@pytest.mark.parametrize("blk,k", [(1, 3), (2, 3), (2, 5), (4, 9), (5, 7), (3, 255)])
+def test_maxpool_window_wider_than_block(blk, k):
+    """A window wider than the block is cut at the block edges (-inf
+    padding): torch float64 max_pool1d with padding (k-1)/2 gives the same,
+    and from k >= 2B-1 on every position holds the block's maximum."""
+    imp = RNG.standard_normal((6, 3, blk))
+    got = oracle.head_mean_maxpool(imp, k)
+    mean = torch.from_numpy(imp).mean(dim=1, keepdim=True)
+    ref = torch.nn.functional.max_pool1d(mean, k, 1, (k - 1) // 2)[:, 0]
+    np.testing.assert_array_equal(got, ref.numpy())
+    if k >= 2 * blk - 1:
+        np.testing.assert_array_equal(
+            got, np.repeat(imp.mean(axis=1).max(axis=1, keepdims=True), blk, axis=1))
 
 
 def test_delta_of_identical_layers_is_zero_and_keeps_first_positions():
