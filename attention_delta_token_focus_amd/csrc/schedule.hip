@@ -3,6 +3,8 @@
 // prefix length; handing the longest ones out first keeps every compute
 // unit busy until the end of a launch (longest-processing-time-first
 // list scheduling).
+#include <limits.h>
+
 #include "focus_internal.hpp"
 
 namespace focus {
@@ -26,7 +28,11 @@ __global__ void __launch_bounds__(1024) lpt_rank_kernel(
   const int i = tid & (kRankMax - 1);       // the sequence ranked
   const int q = tid >> 8;                   // the quarter of the lengths
   const int n4 = (batch + 3) & ~3;
-  if (tid < n4) len[tid] = tid < batch ? cu_prefix[tid + 1] - cu_prefix[tid] : -1;
+  // Padding up to a multiple of four never goes before a sequence, whatever
+  // its length (a non-monotone cu_prefix can make a length negative): the
+  // rank of sequence i counts only real sequences, so the ranks are a
+  // permutation of 0 .. batch-1 and every store below stays inside order[].
+  if (tid < n4) len[tid] = tid < batch ? cu_prefix[tid + 1] - cu_prefix[tid] : INT_MIN;
   __syncthreads();
   int rank = 0;
   if (i < batch) {
@@ -58,9 +64,10 @@ __global__ void __launch_bounds__(1024) lpt_sort_kernel(
   int n2 = 1;
   while (n2 < batch) n2 <<= 1;
   for (int i = tid; i < n2; i += 1024) {
-    uint64_t k = 0;
+    uint64_t k = 0;  // padding: below every real key
     if (i < batch) {
-      const uint32_t len = (uint32_t)(cu_prefix[i + 1] - cu_prefix[i]);
+      // signed length with the sign bit flipped: unsigned order = signed order
+      const uint32_t len = (uint32_t)(cu_prefix[i + 1] - cu_prefix[i]) ^ 0x80000000u;
       k = ((uint64_t)len << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
     }
     key[i] = k;

@@ -70,7 +70,12 @@ const char* focus_last_error(void);
  * call is that step for the work order, done on the device from cu_prefix.
  *
  *  cu_prefix   device int32 [batch+1] as in focus_block_attn_importance.
- *  order       device int32 [batch] output, a permutation of 0..batch-1.
+ *              Only the differences cu_prefix[b+1] - cu_prefix[b] are
+ *              used; they are compared as signed int32, so a non-monotone
+ *              array (negative lengths) still yields a permutation, with
+ *              those sequences last.
+ *  order       device int32 [batch] output, a permutation of 0..batch-1;
+ *              nothing past order[batch-1] is written.
  * Batches above 8192 keep their natural order.
  * Errors: INVALID_ARG (batch < 1, NULL pointer), HIP.
  */
@@ -180,6 +185,9 @@ focus_status focus_block_attn_importance_paged(
  * Fig. 5). Per sequence b and block position j:
  *    Ibar_l[j]  = (1/Hq) sum_h imp_l[b,h,j]              (l = 0, 1)
  *    Itil_l[j]  = max{ Ibar_l[t] : |t - j| <= (pool_k-1)/2, 0 <= t < B }
+ *                 (the window is cut at the block edges, i.e. padded with
+ *                 -inf; pool_k may exceed B, and from pool_k >= 2B-1 on
+ *                 every position takes the block's maximum)
  *    dI[b,j]    = Itil_1[j] - Itil_0[j]
  *    keep[b,j]  = 1 for the min(max(k_keep[b],0),B) largest dI[b,.],
  *                 equal values ordered by lower j first; else 0.

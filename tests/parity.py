@@ -100,6 +100,9 @@ class SelectionReport:
     exact: int = 0
     excused: int = 0
     failed: List[str] = dataclasses.field(default_factory=list)
+    # max abs error per compared quantity (name -> error), for the record
+    errors: Dict[str, float] = dataclasses.field(default_factory=dict)
+    retained_seqs: int = 0    # sequences whose retained attention was compared
 
 
 def check_selection(keep_gpu_b, dI_ref_b, k_b, label, rep: SelectionReport):
@@ -140,34 +143,43 @@ def assert_close(name, got, ref, tol, tight=None, rel_scale=False):
 
 
 def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=None,
-                 further_check: bool = True, bar_scale: float = 1.0) -> SelectionReport:
+                 further_check: bool = True, bar_scale: float = 1.0,
+                 further_seqs: Optional[Sequence[int]] = None) -> SelectionReport:
     """Oracle block-step on sequences `seqs` against the GPU results.
 
     bar_scale multiplies the bars of lse, importance and delta: with scores
     far from O(1) their rounding error grows with the magnitude (one fp32
     ulp of an exponent argument s is |s| * 2^-23); O is a normalised mix
-    and keeps its bars."""
+    and keeps its bars.
+
+    further_seqs: the sequences (a subset of seqs) on which the retained
+    attention of the further layers is compared; default all of seqs."""
     cfg = inp.cfg
     blk, kind = cfg.block, cfg.dtype
     tol = {k: v * (bar_scale if k != "out" else 1.0) for k, v in TOL[kind].items()}
     tight = {k: v * (bar_scale if k != "out" else 1.0) for k, v in TIGHT[kind].items()}
     seqs = list(seqs)
     layers = layers_host if layers_host is not None else inp.layers
-    sub, sub_cu = sub_layers(layers, inp.cu_prefix, blk, seqs)
+    sub, sub_cu = sub_layers(layers[:2], inp.cu_prefix, blk, seqs)
     k_keep = inp.meta.k_keep[seqs]
+    rep = SelectionReport()
     o = [oracle.block_attn_importance(sub[l]["q"], sub[l]["k_blk"], sub[l]["v_blk"],
                                       sub[l]["k_cache"], sub[l]["v_cache"], sub_cu,
                                       blk, cfg.hq, cfg.hkv) for l in (0, 1)]
+    del sub
     for l in (0, 1):
         if res["out"][l] is not None:   # None: importance-only call
-            assert_close(f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
-                         tol["out"], tight["out"], rel_scale=True)
-        assert_close(f"imp L{l}", res["imp"][l][seqs], o[l][1], tol["imp"],
-                     tight["imp"])
+            rep.errors[f"out L{l}"] = assert_close(
+                f"out L{l}", rows_of(res["out"][l], seqs, blk), o[l][0],
+                tol["out"], tight["out"], rel_scale=True)
+        rep.errors[f"imp L{l}"] = assert_close(
+            f"imp L{l}", res["imp"][l][seqs], o[l][1], tol["imp"], tight["imp"])
         if res["lse"][l] is not None:
-            assert_close(f"lse L{l}", res["lse"][l][seqs], o[l][2], tight["lse"])
+            rep.errors[f"lse L{l}"] = assert_close(
+                f"lse L{l}", res["lse"][l][seqs], o[l][2], tight["lse"])
     dI_ref = oracle.importance_delta(o[0][1], o[1][1], cfg.pool_k)
-    assert_close("dI", res["dI"][seqs], dI_ref, tight["dI"])
+    del o
+    rep.errors["dI"] = assert_close("dI", res["dI"][seqs], dI_ref, tight["dI"])
 
     # The GPU's selection is a valid top-K of the GPU's own delta: every
     # kept position beats every evicted one, equal deltas by lower index.
@@ -182,7 +194,6 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
     # Retained sets against the oracle's own selection.
     keep_ref = oracle.topk_keep(dI_ref, k_keep)
     idx_ref, cu_ref = oracle.compact(keep_ref)
-    rep = SelectionReport()
     exact = []
     for i, b in enumerate(seqs):
         before = rep.exact
@@ -205,19 +216,28 @@ def compare_step(inp: workloads.Inputs, res, seqs: Sequence[int], layers_host=No
         assert np.array_equal(mine, ref_j), f"seq {b}: idx {mine} vs {ref_j}"
 
     # Retained attention, oracle on its own retained set; compared on the
-    # sequences whose set matched exactly.
+    # sequences (of further_seqs) whose set matched exactly.
     if further_check and res["ret"]:
-        for li, ret in enumerate(res["ret"]):
-            lay = sub[2 + li]
-            ref = oracle.retained_attn(lay["q"], lay["k_blk"], lay["v_blk"], idx_ref,
-                                       cu_ref, lay["k_cache"], lay["v_cache"], sub_cu,
-                                       blk, cfg.hq, cfg.hkv)
-            if not exact:
-                continue
-            got = np.concatenate([ret[g_cu[seqs[i]]:g_cu[seqs[i] + 1]] for i in exact])
-            want = np.concatenate([ref[cu_ref[i]:cu_ref[i + 1]] for i in exact])
-            assert_close(f"retained L{2 + li}", got, want, tol["out"],
-                         tight["out"], rel_scale=True)
+        pos = {b: i for i, b in enumerate(seqs)}
+        fsel = [pos[b] for b in (seqs if further_seqs is None else further_seqs)]
+        exact_set = set(exact)
+        fex = [i for i in fsel if i in exact_set]
+        fseqs = [seqs[i] for i in fex]
+        rep.retained_seqs = len(fex)
+        if fex:
+            f_idx, f_cu = oracle.compact(keep_ref[fex])
+            worst = 0.0
+            for li, ret in enumerate(res["ret"]):
+                lay, f_pcu = sub_layers([layers[2 + li]], inp.cu_prefix, blk, fseqs)
+                lay = lay[0]
+                ref = oracle.retained_attn(lay["q"], lay["k_blk"], lay["v_blk"], f_idx,
+                                           f_cu, lay["k_cache"], lay["v_cache"], f_pcu,
+                                           blk, cfg.hq, cfg.hkv)
+                got = np.concatenate([ret[g_cu[b]:g_cu[b + 1]] for b in fseqs])
+                err = assert_close(f"retained L{2 + li}", got, ref, tol["out"],
+                                   tight["out"], rel_scale=True)
+                worst = max(worst, err)
+            rep.errors["retained"] = worst
     return rep
 
 

@@ -4,6 +4,9 @@ Small cases run the oracle on every sequence; the full-size workloads are
 checked on sampled sequences that the oracle computes one by one. Every
 call goes through the C ABI of libfocus (via the thin Python binding).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -76,6 +79,11 @@ EDGE = [
     ("long B32", dict(block=32, hq=8, hkv=2), [5000, 4200, 33, 1], [5, 32, 1, 0]),
     ("long B128", dict(block=128, hq=8, hkv=2, pool_k=5), [4500, 0], [32, 128]),
     ("long B48 G8", dict(block=48, hq=16, hkv=2), [4100, 4097, 95], [9, 48, 3]),
+    # pool windows wider than the block (cut at the block edges; from
+    # 2B - 1 on every position takes the block's maximum)
+    ("B2 pool 5", dict(block=2, hq=8, hkv=2, pool_k=5), [100, 3, 0], [1, 1, 2]),
+    ("B4 pool 9 block max", dict(block=4, hq=8, hkv=2, pool_k=9), [40, 0, 7], [1, 2, 4]),
+    ("B5 pool 7", dict(block=5, hq=8, hkv=2, pool_k=7), [33, 64], [2, 3]),
 ]
 
 
@@ -228,6 +236,51 @@ def test_schedule_order(batch):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("batch", [5, 256, 300])
+def test_schedule_non_monotone_prefix(batch):
+    """A non-monotone cu_prefix (negative lengths) still gives a permutation,
+    ordered by the signed lengths, longest first, and nothing is written
+    past order[batch - 1], on both the rank-count and the sort path."""
+    import attention_delta_token_focus_amd as F
+    rng = np.random.default_rng(77 + batch)
+    lens = rng.integers(-60, 60, size=batch)
+    lens[:3] = [-1, -1, 0]
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                         device="cuda")
+    buf = torch.full((batch + 8,), -7, dtype=torch.int32, device="cuda")
+    F.focus_schedule(batch, cu, buf[:batch])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:batch], np.argsort(-lens, kind="stable"))
+    assert (got[batch:] == -7).all()
+
+
+@pytest.mark.parametrize("batch,B", [(1025, 7), (1025, 32), (2049, 16),
+                                     (3000, 128), (3000, 7)])
+def test_compact_past_one_chunk(batch, B):
+    """focus_compact past 1024 sequences (the workgroup walks the batch in
+    chunks of 1024 and carries the offset), with keep bytes other than 0/1,
+    empty and full rows; byte loads (B = 7) and 16-byte row loads."""
+    import attention_delta_token_focus_amd as F
+    rng = np.random.default_rng(batch * 131 + B)
+    vals = rng.integers(1, 256, size=(batch, B)).astype(np.uint8)
+    vals[rng.random((batch, B)) < 0.6] = 0
+    vals[5] = 0
+    vals[1030 % batch] = 255
+    keep = torch.from_numpy(vals).cuda()
+    idx = torch.full((batch * B + 8,), -7, dtype=torch.int32, device="cuda")
+    cu = torch.full((batch + 1,), -7, dtype=torch.int32, device="cuda")
+    F.focus_compact(batch, B, keep, idx, cu)
+    torch.cuda.synchronize()
+    want_idx = np.flatnonzero(vals.ravel() != 0)
+    want_cu = np.concatenate([[0], np.cumsum((vals != 0).sum(axis=1))])
+    got = idx.cpu().numpy()
+    log(f"[compact] batch {batch} B {B}: {len(want_idx)} kept")
+    assert np.array_equal(cu.cpu().numpy(), want_cu)
+    assert np.array_equal(got[:len(want_idx)], want_idx)
+    assert (got[len(want_idx):] == -7).all()
+
+
 def test_visiting_order_does_not_change_results():
     """With order=NULL (the call schedules itself), with focus_schedule's
     order, and with the reversed order, every output is bitwise equal."""
@@ -269,6 +322,111 @@ def test_deterministic_bitwise():
     for k in ("out", "imp", "lse", "ret"):
         for a, b in zip(r1[k], r2[k]):
             assert np.array_equal(a, b), k
+
+
+@pytest.mark.parametrize("over,plens,kk", [
+    (dict(), None, None),
+    (dict(block=128, pool_k=5), [100, 0, 3000], [32, 0, 128]),
+    (dict(block=7), [5, 9, 1, 0], [0, 7, 3, 1]),
+])
+def test_fused_select_equals_two_calls(over, plens, kk):
+    """focus_select must be bit-identical to focus_delta_topk followed by
+    focus_compact (keep, dI, idx, cu_ret)."""
+    import attention_delta_token_focus_amd as F
+    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 40,
+                           **over)
+    log(f"[parity] fused select B={cfg.block} N={cfg.batch}")
+    inp = workloads.make_inputs(cfg, 9, n_layers=2, prefix_lens=plens, k_keep=kk)
+    s1, r1 = parity.run_gpu(inp)
+    step = s1
+    keep2 = torch.zeros_like(step.keep)
+    dI2 = torch.zeros_like(step.dI)
+    idx2 = torch.full_like(step.idx, -7)
+    cu2 = torch.zeros_like(step.cu_ret)
+    dm = step.dims
+    F.focus_delta_topk(dm.batch, dm.block, dm.hq, dm.pool_k, step.imp[0], step.imp[1],
+                       step.k_keep, keep2, dI2)
+    F.focus_compact(dm.batch, dm.block, keep2, idx2, cu2)
+    torch.cuda.synchronize()
+    assert torch.equal(keep2.cpu(), torch.from_numpy(r1["keep"]))
+    assert torch.equal(dI2.cpu(), torch.from_numpy(r1["dI"]))
+    assert torch.equal(cu2.cpu(), torch.from_numpy(r1["cu_ret"]))
+    assert np.array_equal(idx2.cpu().numpy()[:step.n_ret], r1["idx"])
+
+
+def _record(entry):
+    """Logs one full-size parity record; appended as a JSON line to the file
+    named by FOCUS_PARITY_RECORD when that is set."""
+    line = json.dumps(entry, sort_keys=True)
+    log(f"[record] {line}")
+    path = os.environ.get("FOCUS_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+def _full_size(name, cfg_name, n_layers=None, further_pick=None):
+    """Every sequence of a full-size workload, in the launch configuration
+    the benchmark times, against the oracle: S1 on both layers (O, I, lse),
+    the delta, the selection (bit-exact, or excused by the 1e-4 gap rule),
+    the compaction, and the retained attention of every further layer on the
+    exactly matched sequences (of further_pick's sequences, if given)."""
+    cfg = workloads.get(cfg_name)
+    log(f"[parity] full size {name}: generating on the device")
+    inp = workloads.make_inputs(cfg, 0, device="cuda", n_layers=n_layers)
+    plen = inp.meta.prefix_lens
+    step, res = parity.run_gpu(inp, layers_dev=inp.layers)
+    further = None if further_pick is None else sorted(set(further_pick(plen)))
+    if further is not None:
+        log(f"  retained layers on sequences {further} "
+            f"(P_b {[int(plen[s]) for s in further]})")
+    rep = parity.compare_step(inp, res, range(cfg.batch), layers_host=inp.layers,
+                              further_seqs=further)
+    # properties of the whole batch
+    kb = np.clip(inp.meta.k_keep, 0, cfg.block)
+    assert np.array_equal(res["keep"].sum(axis=1), kb)
+    assert np.array_equal(np.diff(res["cu_ret"]), kb)
+    imp_sum = res["imp"][0].sum(axis=2)
+    assert (imp_sum > 0).all() and (imp_sum <= cfg.block * (1 + 1e-5)).all()
+    assert rep.exact + rep.excused == cfg.batch
+    _record(dict(config=cfg.name, sequences=cfg.batch, exact=rep.exact,
+                 excused=rep.excused, further_layers=len(res["ret"]),
+                 retained_sequences_compared=rep.retained_seqs,
+                 max_abs_err={k: float(f"{v:.3e}") for k, v in rep.errors.items()}))
+    del inp, step
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_c3_full_size_every_sequence():
+    _full_size("c3", "c3", n_layers=3)
+
+
+@pytest.mark.timeout(900)
+def test_c5_full_size_every_sequence():
+    """All 128 sequences through S1-S5a; 16 of them (longest, shortest and
+    14 evenly spaced) through all 34 further layers."""
+    def pick(p, n=16):
+        out = [int(np.argmax(p)), int(np.argmin(p))]
+        for b in range(0, len(p), 7):
+            if len(out) < n and b not in out:
+                out.append(b)
+        return out
+    _full_size("c5", "c5", further_pick=pick)
+
+
+@pytest.mark.timeout(900)
+def test_c4_full_size_every_sequence():
+    """B = 128 (four block tiles, four workgroups per KV head), fixed
+    2048-token prefixes."""
+    _full_size("c4", "c4", n_layers=3)
+
+
+@pytest.mark.timeout(900)
+def test_c6_full_size_every_sequence():
+    """B = 64 (two block tiles, two workgroups per KV head), lognormal
+    prefixes."""
+    _full_size("c6", "c6", n_layers=3)
 
 
 @pytest.mark.parametrize("over,plens,kk", [
