@@ -2,7 +2,8 @@
 
 Order of calls per step (one stream, no host synchronisation):
   focus_schedule (longest-prefix-first visiting order, shared by the
-  attention calls of the step);
+  attention calls of the step; with shared_order=False there is no such
+  call and each attention call computes the order itself, order=NULL);
   focus_block_attn_importance on layer 0, then on layer 1 (with
   l1_output=False layer 1 gets out=NULL: importance and lse only, no V
   read, no P V product);
@@ -57,9 +58,12 @@ class FocusStep:
                  k_keep_host: Sequence[int], n_further: int = 0,
                  device="cuda", with_lse: bool = False, fused: bool = True,
                  l1_output: bool = True, masked=None, rules: int = 0,
-                 yield_hist=None, alpha: float = 1.5):
+                 yield_hist=None, alpha: float = 1.5, shared_order: bool = True):
         self.dims = dims
         self.fused = fused
+        # shared_order=False: no focus_schedule call; every attention call
+        # gets order=NULL and writes the visiting order into its workspace
+        self.shared_order = shared_order
         self.l1_output = l1_output
         self.constrained = (masked is not None or rules != 0
                             or yield_hist is not None)
@@ -113,7 +117,11 @@ class FocusStep:
 
     # -- single calls -----------------------------------------------------
     def schedule(self, stream=None) -> None:
-        focus_schedule(self.dims.batch, self.cu_prefix, self.order, stream)
+        if self.shared_order:
+            focus_schedule(self.dims.batch, self.cu_prefix, self.order, stream)
+
+    def _order(self):
+        return self.order if self.shared_order else None
 
     def block_attn(self, layer: Dict[str, torch.Tensor], which: int,
                    stream=None) -> None:
@@ -124,7 +132,7 @@ class FocusStep:
             layer["v_blk"] if self.out[which] is not None else None,
             layer["k_cache"],
             layer["v_cache"] if self.out[which] is not None else None,
-            self.cu_prefix, self.order,
+            self.cu_prefix, self._order(),
             self.max_prefix, self.out[which], self.imp[which],
             self.lse[which], self.ws, self.ws_bytes, stream)
 
@@ -160,7 +168,7 @@ class FocusStep:
             dtype_code(dm.dtype), dm.batch, dm.block, dm.hq, dm.hkv,
             dm.head_dim, dm.scale, layer["q"], layer["k_blk"], layer["v_blk"],
             self.idx, self.cu_ret, self.n_ret, self.max_ret,
-            layer["k_cache"], layer["v_cache"], self.cu_prefix, self.order,
+            layer["k_cache"], layer["v_cache"], self.cu_prefix, self._order(),
             self.max_prefix, self.ret_out[which], self.ws, self.ws_bytes,
             stream)
 

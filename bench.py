@@ -195,6 +195,34 @@ def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
     }
 
 
+def time_order_per_call(cfg, inp, dims, n_further, args):
+    """The same step without focus_schedule: every attention call gets
+    order=NULL and writes the longest-prefix-first order into its workspace
+    first (one more small launch per attention call), as a caller that
+    does not share one visiting order between the calls of a step."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=n_further,
+                     shared_order=False)
+    layers = inp.layers
+    for _ in range(max(1, args.warmup // 2)):
+        step.run(layers)
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        step.run(layers)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    return {
+        "block_steps_per_s": round(cfg.batch * args.steps / (total_ms / 1e3), 1),
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "attention_calls_per_step": 2 + n_further,
+    }
+
+
 def paged_pool(kv, cu, page_size, seed):
     """The same prefix rows in shuffled pages of page_size tokens (one
     gather on the device). Returns pool, page_table, pages_per_seq."""
@@ -475,6 +503,8 @@ def main() -> int:
                 cfg, inp, dims, n_further, args),
             "paged_prefix_kv": time_paged(cfg, inp, dims, args, plen),
             "dynamic_budget_reading": time_dynamic_select(cfg, inp, dims, args),
+            "order_per_attention_call": time_order_per_call(
+                cfg, inp, dims, n_further, args),
         }
 
     stream_ref = stream_read_reference(args)
