@@ -431,76 +431,6 @@ def test_c6_full_size_every_sequence():
 
 @pytest.mark.parametrize("over,plens,kk", [
     (dict(), None, None),
-    (dict(block=128, pool_k=5), [100, 0, 3000], [32, 0, 128]),
-    (dict(block=7), [5, 9, 1, 0], [0, 7, 3, 1]),
-])
-def test_fused_select_equals_two_calls(over, plens, kk):
-    """focus_select must be bit-identical to focus_delta_topk followed by
-    focus_compact (keep, dI, idx, cu_ret)."""
-    import attention_delta_token_focus_amd as F
-    cfg = workloads.scaled(workloads.get("c3"), batch=len(plens) if plens else 40,
-                           **over)
-    log(f"[parity] fused select B={cfg.block} N={cfg.batch}")
-    inp = workloads.make_inputs(cfg, 9, n_layers=2, prefix_lens=plens, k_keep=kk)
-    s1, r1 = parity.run_gpu(inp)
-    step = s1
-    keep2 = torch.zeros_like(step.keep)
-    dI2 = torch.zeros_like(step.dI)
-    idx2 = torch.full_like(step.idx, -7)
-    cu2 = torch.zeros_like(step.cu_ret)
-    dm = step.dims
-    F.focus_delta_topk(dm.batch, dm.block, dm.hq, dm.pool_k, step.imp[0], step.imp[1],
-                       step.k_keep, keep2, dI2)
-    F.focus_compact(dm.batch, dm.block, keep2, idx2, cu2)
-    torch.cuda.synchronize()
-    assert torch.equal(keep2.cpu(), torch.from_numpy(r1["keep"]))
-    assert torch.equal(dI2.cpu(), torch.from_numpy(r1["dI"]))
-    assert torch.equal(cu2.cpu(), torch.from_numpy(r1["cu_ret"]))
-    assert np.array_equal(idx2.cpu().numpy()[:step.n_ret], r1["idx"])
-
-
-def _full_size(name, cfg_name, seqs_pick, n_layers=None):
-    cfg = workloads.get(cfg_name)
-    log(f"[parity] full size {name}: generating on the device")
-    inp = workloads.make_inputs(cfg, 0, device="cuda", n_layers=n_layers)
-    plen = inp.meta.prefix_lens
-    seqs = sorted(set(seqs_pick(plen)))
-    log(f"  sequences checked: {seqs} (P_b {[int(plen[s]) for s in seqs]})")
-    step, res = parity.run_gpu(inp, layers_dev=inp.layers)
-    parity.compare_step(inp, res, seqs, layers_host=inp.layers)
-    # properties that hold at any size
-    kb = np.clip(inp.meta.k_keep, 0, cfg.block)
-    assert np.array_equal(res["keep"].sum(axis=1), kb)
-    assert np.array_equal(np.diff(res["cu_ret"]), kb)
-    imp_sum = res["imp"][0].sum(axis=2)
-    assert (imp_sum > 0).all() and (imp_sum <= cfg.block * (1 + 1e-5)).all()
-    del inp, step
-    torch.cuda.empty_cache()
-
-
-def test_c3_full_size_sampled():
-    _full_size("c3", "c3", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 0,
-                                      17, 128, 255], n_layers=3)
-
-
-def test_c5_full_size_sampled():
-    _full_size("c5", "c5", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 64])
-
-
-def test_c4_full_size_sampled():
-    """B = 128 (four block tiles, four workgroups per KV head), fixed
-    2048-token prefixes: first, middle and last sequence."""
-    _full_size("c4", "c4", lambda p: [0, 31, 63])
-
-
-def test_c6_full_size_sampled():
-    """B = 64 (two block tiles, two workgroups per KV head), lognormal
-    prefixes: longest, shortest and two fixed sequences."""
-    _full_size("c6", "c6", lambda p: [int(np.argmax(p)), int(np.argmin(p)), 0, 100])
-
-
-@pytest.mark.parametrize("over,plens,kk", [
-    (dict(), None, None),
     (dict(block=128, pool_k=5), [100, 0, 2100], [32, 0, 128]),
     (dict(block=7), [5, 90, 1, 0], [0, 7, 3, 1]),
     (dict(block=48, hq=16, hkv=2), [40, 333], [9, 48]),
