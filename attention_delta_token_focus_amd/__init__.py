@@ -22,7 +22,7 @@ __all__ = [
     "FocusError", "lib", "lib_path", "dtype_code", "focus_version",
     "focus_status_string", "focus_last_error", "focus_schedule",
     "focus_block_attn_importance_workspace", "focus_block_attn_importance",
-    "focus_block_attn_importance_paged",
+    "focus_block_attn_importance_paged", "focus_block_attn_importance_noalloc",
     "focus_delta_topk", "focus_compact", "focus_select", "focus_select_masked",
     "focus_select_dynamic",
     "focus_retained_attn_workspace", "focus_retained_attn",
@@ -66,6 +66,9 @@ _SIGS = {
     "focus_block_attn_importance_paged": (
         _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _I,
              _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "focus_block_attn_importance_noalloc": (
+        _I, [_I, _I, _I, _I, _I, _I, _c.c_float, _P, _P, _P, _P, _P, _P, _I,
+             _P, _P, _P, _P]),
     "focus_delta_topk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "focus_compact": (_I, [_I, _I, _P, _P, _P, _P]),
     "focus_select": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -171,6 +174,18 @@ def focus_block_attn_importance(dt, batch, B, Hq, Hkv, d, scale, q, k_blk,
         _ptr(imp, "imp"), _ptr(lse, "lse", True),
         _ptr(workspace, "workspace", True), workspace_bytes,
         _stream(stream)))
+
+
+def focus_block_attn_importance_noalloc(dt, batch, B, Hq, Hkv, d, scale, q,
+                                        k_blk, v_blk, k_cache, v_cache,
+                                        cu_prefix, max_prefix, out, imp,
+                                        lse=None, stream=None) -> None:
+    _check(lib.focus_block_attn_importance_noalloc(
+        dtype_code(dt), batch, B, Hq, Hkv, d, float(scale),
+        _ptr(q, "q"), _ptr(k_blk, "k_blk"), _ptr(v_blk, "v_blk", True),
+        _ptr(k_cache, "k_cache", True), _ptr(v_cache, "v_cache", True),
+        _ptr(cu_prefix, "cu_prefix"), max_prefix, _ptr(out, "out", True),
+        _ptr(imp, "imp"), _ptr(lse, "lse", True), _stream(stream)))
 
 
 def focus_block_attn_importance_paged(dt, batch, B, Hq, Hkv, d, scale, q,

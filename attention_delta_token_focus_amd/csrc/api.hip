@@ -5,10 +5,20 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "focus.h"
 #include "focus_internal.hpp"
+
+// Device scratch of focus_block_attn_importance_noalloc: the visiting order
+// that call writes before its attention launch (what the workspace holds
+// for focus_block_attn_importance with order = NULL). Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// In host code `scratch` is only a host-side handle: its device address
+// comes from hipGetSymbolAddress (see noalloc_scratch below).
+constexpr int kNoAllocMaxBatch = 65536;  // sequences (256 KiB of int32)
+static __device__ __align__(256) int32_t scratch[kNoAllocMaxBatch];
 
 namespace {
 
@@ -129,12 +139,45 @@ focus_status check_paging(const char* fn, const Paging& pg, int max_prefix) {
   return FOCUS_OK;
 }
 
+// Device address of `scratch` on the device that `stream` belongs to,
+// looked up once per device (with that device current) and cached.
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mu;
+int32_t* scratch_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void* stream, int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice((hipStream_t)stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// static_scratch: the order goes to the library's own device scratch
+// (focus_block_attn_importance_noalloc); workspace is then ignored.
 focus_status block_attn_impl(
     const char* fn, focus_dtype dt, int batch, int B, int Hq, int Hkv, int d,
     float scale, const void* q, const void* k_blk, const void* v_blk,
     const void* k_cache, const void* v_cache, const Paging* pg,
     const int32_t* cu_prefix, const int32_t* order, int max_prefix, void* out,
-    float* imp, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    float* imp, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+    bool static_scratch = false) {
   try {
     focus_status st = check_attn_shape(fn, dt, batch, B, Hq, Hkv, d, max_prefix);
     if (st != FOCUS_OK) return st;
@@ -159,6 +202,17 @@ focus_status block_attn_impl(
     size_t need = 0;
     st = focus_block_attn_importance_workspace(batch, B, Hq, Hkv, d, max_prefix, &need);
     if (st != FOCUS_OK) return st;
+    if (static_scratch) {
+      if (batch > kNoAllocMaxBatch)
+        return fail(FOCUS_ERR_WORKSPACE,
+                    "%s: batch %d exceeds the static scratch (%d sequences)", fn, batch,
+                    kNoAllocMaxBatch);
+      int32_t* ptr = nullptr;
+      const hipError_t he = noalloc_scratch(stream, &ptr);
+      if (he != hipSuccess) return hip_status(he, "static scratch lookup");
+      workspace = ptr;
+      workspace_bytes = sizeof(int32_t) * (size_t)kNoAllocMaxBatch;
+    }
     if (order != nullptr) need = 0;  // the workspace only holds our own order
     if (workspace_bytes < need || (need > 0 && workspace == nullptr))
       return fail(FOCUS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed",
@@ -325,6 +379,17 @@ focus_status focus_block_attn_importance(
                          scale, q, k_blk, v_blk, k_cache, v_cache, nullptr,
                          cu_prefix, order, max_prefix, out, imp, lse, workspace,
                          workspace_bytes, stream);
+}
+
+focus_status focus_block_attn_importance_noalloc(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk, const void* k_cache,
+    const void* v_cache, const int32_t* cu_prefix, int max_prefix, void* out,
+    float* imp, float* lse, void* stream) {
+  return block_attn_impl("focus_block_attn_importance_noalloc", dt, batch, B, Hq, Hkv,
+                         d, scale, q, k_blk, v_blk, k_cache, v_cache, nullptr,
+                         cu_prefix, nullptr, max_prefix, out, imp, lse, nullptr, 0,
+                         stream, /*static_scratch=*/true);
 }
 
 focus_status focus_block_attn_importance_paged(

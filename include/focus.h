@@ -11,7 +11,8 @@
  * --------------------------------
  *  - Every array pointer is caller-owned DEVICE memory, contiguous,
  *    row-major and 16-byte aligned. The library keeps no pointer after a
- *    call returns, allocates no device memory and holds no global state.
+ *    call returns and allocates no device memory; its only global state is
+ *    the static scratch of focus_block_attn_importance_noalloc.
  *  - Outputs must not alias inputs.
  *  - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
  *    default stream) and never synchronises. Device-side faults surface at
@@ -141,6 +142,31 @@ focus_status focus_block_attn_importance(
     const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
     const int32_t* order, int max_prefix, void* out, float* imp, float* lse,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * focus_block_attn_importance with order = NULL, for callers that cannot
+ * allocate device memory or hand in a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same
+ * computation and outputs, bit for bit; arguments as there, without order,
+ * workspace and workspace_bytes.
+ *
+ * The longest-prefix-first visiting order this call computes goes to a
+ * static device array inside the library instead of a workspace: at most
+ * 65536 sequences (256 KiB of int32), held on every GPU the library runs
+ * on until the process ends. The call allocates nothing (no hipMalloc, no
+ * hipFree). The scratch of the stream's device is looked up once, on the
+ * first call on that device. Every call on one GPU shares that GPU's
+ * scratch and overwrites it: two calls that overlap in time on the same
+ * GPU (different streams, or threads without ordering) race, so
+ * concurrent callers must serialise, e.g. by using one stream.
+ * Errors: as focus_block_attn_importance; WORKSPACE for batch > 65536;
+ * HIP if the stream's device or the scratch address cannot be obtained.
+ */
+focus_status focus_block_attn_importance_noalloc(
+    focus_dtype dt, int batch, int B, int Hq, int Hkv, int d, float scale,
+    const void* q, const void* k_blk, const void* v_blk,
+    const void* k_cache, const void* v_cache, const int32_t* cu_prefix,
+    int max_prefix, void* out, float* imp, float* lse, void* stream);
 
 /*
  * focus_block_attn_importance over a paged prefix KV cache: the same

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(F.lib, name), name
         assert callable(getattr(F, name)), name
@@ -113,6 +113,35 @@ def _paged(**kw):
 def test_paged_block_attention_rejects_bad_arguments(kw, code):
     assert _paged(**kw) == code
     assert F.focus_last_error().startswith("focus_block_attn_importance_paged")
+
+
+def _noalloc(**kw):
+    a = dict(dt=1, batch=2, B=32, Hq=32, Hkv=8, d=128, scale=0.0, q=FAKE,
+             k_blk=FAKE, v_blk=FAKE, k_cache=FAKE, v_cache=FAKE,
+             cu_prefix=FAKE, max_prefix=16, out=FAKE, imp=FAKE, lse=None,
+             stream=None)
+    a.update(kw)
+    return F.lib.focus_block_attn_importance_noalloc(
+        a["dt"], a["batch"], a["B"], a["Hq"], a["Hkv"], a["d"], a["scale"],
+        a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"],
+        a["cu_prefix"], a["max_prefix"], a["out"], a["imp"], a["lse"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), F.FOCUS_ERR_INVALID_ARG),
+    (dict(B=129), F.FOCUS_ERR_INVALID_ARG),
+    (dict(Hq=30), F.FOCUS_ERR_UNSUPPORTED),
+    (dict(q=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(imp=FAKE + 4), F.FOCUS_ERR_INVALID_ARG),
+    (dict(v_cache=None), F.FOCUS_ERR_INVALID_ARG),
+    (dict(batch=65537), F.FOCUS_ERR_WORKSPACE),
+])
+def test_noalloc_block_attention_rejects_bad_arguments(kw, code):
+    """Argument errors, and a batch beyond the static scratch, are reported
+    before any device call."""
+    assert _noalloc(**kw) == code
+    assert F.focus_last_error()
 
 
 def test_paged_retained_attention_checks_pages():
