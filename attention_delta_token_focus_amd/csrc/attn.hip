@@ -107,8 +107,12 @@ __device__ __forceinline__ T chunk_elem(const u32x4& v, int e) {
   }
 }
 
+// Two workgroups per CU, except fp32 with head_dim 128: its fp32 operand
+// and LDS tiles need more registers than two workgroups per CU leave
+// (the compiler reaches one), so that instantiation asks for one.
 template <bool RET, typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) attn_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kThreads, (sizeof(T) == 4 && D == 128) ? 1 : 2)
+    attn_kernel(const AttnArgs a) {
   using M = Mfma<T>;
   using G = Geo<T, D>;
   using frag = typename M::frag;

@@ -96,6 +96,8 @@ hipError_t launch_delta_topk(int batch, int B, int Hq, int pool_k,
                              const int32_t* k_keep, const float* yield_hist,
                              float alpha, int32_t* k_used, uint8_t* keep,
                              uint8_t* cand, float* dI, hipStream_t s);
+// Largest batch the fused delta/top-K + compaction kernel takes.
+constexpr int kFusedSelectMax = 4096;
 hipError_t launch_select(int batch, int B, int Hq, int pool_k,
                          const float* imp0, const float* imp1,
                          const int32_t* k_keep, uint8_t* keep, float* dI,

@@ -269,6 +269,9 @@ __global__ void __launch_bounds__(64) select_kernel(
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   int off = 0;
+  // unrolled so that several budget loads are in flight (the host sends
+  // batches above kFusedSelectMax to the two-launch path instead)
+#pragma unroll 8
   for (int c = 0; c < b; c += 64) {
     const int i = c + lane;
     if (i < b) off += min(max(k_keep[i], 0), B);
@@ -408,6 +411,16 @@ hipError_t launch_select(int batch, int B, int Hq, int pool_k,
                          const float* imp0, const float* imp1,
                          const int32_t* k_keep, uint8_t* keep, float* dI,
                          int32_t* idx, int32_t* cu_ret, hipStream_t s) {
+  // Each wavefront of the fused kernel sums the budgets of all earlier
+  // sequences (O(batch) per sequence); past kFusedSelectMax sequences the
+  // two launches (O(batch) in total) are faster, with the same outputs.
+  if (batch > kFusedSelectMax) {
+    const hipError_t e = launch_delta_topk(batch, B, Hq, pool_k, imp0, imp1, nullptr, 0,
+                                           k_keep, nullptr, 0.f, nullptr, keep, nullptr,
+                                           dI, s);
+    if (e != hipSuccess) return e;
+    return launch_compact(batch, B, keep, idx, cu_ret, s);
+  }
   if (B <= 64) {
     hipLaunchKernelGGL(select_kernel<1>, dim3(batch), dim3(64), 0, s, batch, B, Hq,
                        (pool_k - 1) / 2, imp0, imp1, k_keep, keep, dI, idx, cu_ret);

@@ -253,7 +253,8 @@ focus_status focus_compact(int batch, int B, const uint8_t* keep,
  * tokens' index list for the remaining layers ("The pith"). Each sequence's
  * offset in idx is the sum of min(max(K_b', 0), B) over the sequences
  * before it, which is what top-K keeps. One kernel instead of two on the
- * per-step path; the per-sequence offset sum costs O(batch) per sequence.
+ * per-step path; the per-sequence offset sum costs O(batch) per sequence,
+ * so batches above 4096 sequences run the two kernels instead.
  *
  *  idx     int32, capacity batch*B; cu_ret int32 [batch+1]; others as in
  *          focus_delta_topk. dI may be NULL.

@@ -354,6 +354,43 @@ def test_fused_select_equals_two_calls(over, plens, kk):
     assert np.array_equal(idx2.cpu().numpy()[:step.n_ret], r1["idx"])
 
 
+@pytest.mark.parametrize("batch,B", [(4096, 32), (4097, 32), (9000, 7)])
+def test_select_large_batches(batch, B):
+    """focus_select on both sides of the switch from the one-launch kernel
+    (up to 4096 sequences) to delta/top-K + compaction: the delta against
+    the oracle's, the selection against the oracle's (bit-exact, or excused
+    by the gap rule), the compaction against the kept flags and budgets."""
+    import attention_delta_token_focus_amd as F
+    import oracle
+    rng = np.random.default_rng(batch + B)
+    hq, pool = 8, 3
+    imp0 = rng.random((batch, hq, B), dtype=np.float32)
+    imp1 = rng.random((batch, hq, B), dtype=np.float32)
+    kk = rng.integers(-2, B + 3, size=batch).astype(np.int32)
+    dev = lambda x: torch.from_numpy(x).cuda()
+    keep = torch.full((batch, B), 7, dtype=torch.uint8, device="cuda")
+    dI = torch.empty((batch, B), device="cuda")
+    idx = torch.full((batch * B + 4,), -7, dtype=torch.int32, device="cuda")
+    cu = torch.empty((batch + 1,), dtype=torch.int32, device="cuda")
+    log(f"[select] batch {batch} B {B}")
+    F.focus_select(batch, B, hq, pool, dev(imp0), dev(imp1), dev(kk), keep, dI, idx, cu)
+    torch.cuda.synchronize()
+    dI_ref = oracle.importance_delta(imp0.astype(np.float64), imp1.astype(np.float64), pool)
+    parity.assert_close("dI", dI.cpu().numpy(), dI_ref, 1e-6)
+    keep_h = keep.cpu().numpy()
+    rep = parity.SelectionReport()
+    for b in range(batch):
+        parity.check_selection(keep_h[b], dI_ref[b], kk[b], f"seq {b}", rep)
+    log(f"  selection: {rep.exact} exact, {rep.excused} excused")
+    assert not rep.failed, rep.failed[:3]
+    kb = np.clip(kk, 0, B)
+    assert np.array_equal(cu.cpu().numpy(), np.concatenate([[0], np.cumsum(kb)]))
+    got = idx.cpu().numpy()
+    n = int(kb.sum())
+    assert np.array_equal(got[:n], np.flatnonzero(keep_h.ravel()))
+    assert (got[n:] == -7).all()
+
+
 def _record(entry):
     """Logs one full-size parity record; appended as a JSON line to the file
     named by FOCUS_PARITY_RECORD when that is set."""
