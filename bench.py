@@ -195,30 +195,41 @@ def time_l1_importance_only(cfg, inp, dims, n_further, args, plen):
     }
 
 
-def time_order_per_call(cfg, inp, dims, n_further, args):
-    """The same step without focus_schedule: every attention call gets
+def time_order_per_call(cfg, inp, dims, n_further, args, rounds=4):
+    """The step with one shared visiting order (focus_schedule, as timed
+    above) against the same step without it: every attention call gets
     order=NULL and writes the longest-prefix-first order into its workspace
-    first (one more small launch per attention call), as a caller that
-    does not share one visiting order between the calls of a step."""
+    first (one more small launch per attention call). The two forms
+    alternate in blocks of steps, so that clock drift over the run does not
+    favour either; medians of the blocks."""
     from attention_delta_token_focus_amd.step import FocusStep
-    step = FocusStep(dims, inp.cu_prefix, inp.meta.k_keep, n_further=n_further,
-                     shared_order=False)
+    steps = {shared: FocusStep(dims, inp.cu_prefix, inp.meta.k_keep,
+                               n_further=n_further, shared_order=shared)
+             for shared in (True, False)}
     layers = inp.layers
-    for _ in range(max(1, args.warmup // 2)):
-        step.run(layers)
+    for st in steps.values():
+        for _ in range(max(1, args.warmup // 2)):
+            st.run(layers)
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    per = max(1, args.steps // rounds)
+    ms = {True: [], False: []}
     torch.cuda.synchronize()
-    t0.record(stream)
-    for s in range(args.steps):
-        step.run(layers)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    for r in range(2 * rounds):
+        shared = (r % 2 == 0) == (r // 2 % 2 == 0)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(per):
+            steps[shared].run(layers)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms[shared].append(t0.elapsed_time(t1) / per)
+    shared_ms = float(np.median(ms[True]))
+    own_ms = float(np.median(ms[False]))
     return {
-        "block_steps_per_s": round(cfg.batch * args.steps / (total_ms / 1e3), 1),
-        "ms_per_step": round(total_ms / args.steps, 4),
+        "ms_per_step_shared_order": round(shared_ms, 4),
+        "ms_per_step_order_per_call": round(own_ms, 4),
+        "block_steps_per_s_order_per_call": round(cfg.batch / (own_ms / 1e3), 1),
         "attention_calls_per_step": 2 + n_further,
     }
 
