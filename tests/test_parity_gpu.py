@@ -435,6 +435,125 @@ def _full_size(name, cfg_name, n_layers=None, further_pick=None):
 
 
 @pytest.mark.timeout(900)
+def test_c3_full_size_variants():
+    """The variant rows at the full c3 size, in the launch configuration the
+    benchmark times them: paged prefix KV (shuffled 64-token pages) bitwise
+    equal to the packed call; layer 1 without O bitwise equal (importance,
+    lse) to the call with O; the masked-candidate selection with both
+    structural rules and the dynamic-budget reading against the oracle
+    applied to the GPU's own delta (the delta itself is compared with the
+    oracle's on every sequence by test_c3_full_size_every_sequence), with
+    their compaction; retained attention on the constrained retained set of
+    sampled sequences against the oracle."""
+    import attention_delta_token_focus_amd as F
+    import oracle
+    from tests.test_oracle_constrained import _characterise
+    cfg = workloads.get("c3")
+    log("[parity] full size c3 variants: generating on the device")
+    inp = workloads.make_inputs(cfg, 0, device="cuda", n_layers=3)
+    lay = inp.layers
+    step, res = parity.run_gpu(inp, layers_dev=lay)
+    dm = step.dims
+    n, blk = cfg.batch, cfg.block
+    cu = np.asarray(inp.cu_prefix, dtype=np.int64)
+    code = F.dtype_code(dm.dtype)
+    # paged prefix, layer 0 with O
+    L = lay[0]
+    kp, table, pps = _paged_pool(L["k_cache"], cu, 64, 7)
+    vp, _, _ = _paged_pool(L["v_cache"], cu, 64, 7)
+    out = torch.empty_like(step.out[0])
+    imp = torch.empty_like(step.imp[0])
+    lse = torch.empty_like(step.lse[0])
+    F.focus_block_attn_importance_paged(
+        code, n, blk, dm.hq, dm.hkv, dm.head_dim, 0.0, L["q"], L["k_blk"], L["v_blk"],
+        kp, vp, table, 64, pps, step.cu_prefix, step.order, step.max_prefix, out, imp,
+        lse, step.ws, step.ws_bytes)
+    # layer 1 without O
+    L1 = lay[1]
+    imp1 = torch.empty_like(step.imp[1])
+    lse1 = torch.empty_like(step.lse[1])
+    F.focus_block_attn_importance(
+        code, n, blk, dm.hq, dm.hkv, dm.head_dim, 0.0, L1["q"], L1["k_blk"], None,
+        L1["k_cache"], None, step.cu_prefix, step.order, step.max_prefix, None, imp1,
+        lse1, step.ws, step.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out, step.out[0]) and torch.equal(imp, step.imp[0])
+    assert torch.equal(lse, step.lse[0])
+    assert torch.equal(imp1, step.imp[1]) and torch.equal(lse1, step.lse[1])
+    del kp, vp
+    # masked candidates + both rules, then the dynamic-budget reading
+    masked = workloads.draw_masked(cfg, 0)
+    yld = workloads.draw_yield(cfg, 0)
+    dI_gpu = res["dI"].astype(np.float64)
+    dev = lambda x, t: torch.as_tensor(np.asarray(x), dtype=t, device="cuda")
+    m_dev = dev(masked, torch.uint8)
+    counts = {}
+    for kind in ("masked", "dynamic"):
+        keep = torch.empty((n, blk), dtype=torch.uint8, device="cuda")
+        cand = torch.empty_like(keep)
+        dI = torch.empty((n, blk), device="cuda")
+        idx = torch.full((n * blk,), -7, dtype=torch.int32, device="cuda")
+        cu_ret = torch.empty((n + 1,), dtype=torch.int32, device="cuda")
+        if kind == "masked":
+            kk = inp.meta.k_keep
+            F.focus_select_masked(n, blk, dm.hq, dm.pool_k, step.imp[0], step.imp[1], m_dev,
+                                  step.k_keep, 3, keep, cand, dI, idx, cu_ret)
+        else:
+            k_used = torch.empty((n,), dtype=torch.int32, device="cuda")
+            F.focus_select_dynamic(n, blk, dm.hq, dm.pool_k, step.imp[0], step.imp[1], m_dev,
+                                   dev(yld, torch.float32), 1.5, 3, keep, k_used, cand, dI,
+                                   idx, cu_ret)
+        torch.cuda.synchronize()
+        assert torch.equal(dI.cpu(), torch.from_numpy(res["dI"]))
+        if kind == "dynamic":
+            kk = k_used.cpu().numpy()
+            k_ref = oracle.dynamic_budget(dI_gpu, masked, yld, 1.5)
+            for b in np.flatnonzero(kk != k_ref):
+                v = dI_gpu[b][np.asarray(masked[b]).astype(bool)]
+                margin = float(np.min(np.abs(v - (v.mean() + v.std()))))
+                assert margin < parity.GAP, (b, kk[b], k_ref[b], margin)
+            counts["dynamic_budget_equal"] = int((kk == k_ref).sum())
+        keep_h, cand_h = keep.cpu().numpy(), cand.cpu().numpy()
+        keep_ref, cand_ref = oracle.select_constrained(dI_gpu, masked, kk, True, True)
+        assert np.array_equal(keep_h, keep_ref) and np.array_equal(cand_h, cand_ref)
+        for b in range(0, n, 17):
+            _characterise(dI_gpu[b], masked[b], int(kk[b]), True, True, keep_h[b], cand_h[b])
+        cnt = keep_h.sum(axis=1)
+        cu_h = cu_ret.cpu().numpy()
+        assert np.array_equal(cu_h, np.concatenate([[0], np.cumsum(cnt)]))
+        tot = int(cu_h[-1])
+        assert np.array_equal(idx.cpu().numpy()[:tot], np.flatnonzero(keep_h.ravel()))
+        counts[kind + "_retained_tokens"] = tot
+        log(f"  {kind}: {tot} retained tokens, selection equal to the oracle's on all "
+            f"{n} sequences")
+    # retained attention on the last (dynamic) constrained set, sampled sequences
+    L2 = lay[2]
+    ret = torch.empty((n * blk, dm.hq, dm.head_dim), dtype=dm.dtype, device="cuda")
+    F.focus_retained_attn(code, n, blk, dm.hq, dm.hkv, dm.head_dim, 0.0, L2["q"],
+                          L2["k_blk"], L2["v_blk"], idx, cu_ret, n * blk, blk,
+                          L2["k_cache"], L2["v_cache"], step.cu_prefix, step.order,
+                          step.max_prefix, ret, step.ws, step.ws_bytes)
+    torch.cuda.synchronize()
+    plen = inp.meta.prefix_lens
+    seqs = sorted({int(np.argmax(plen)), int(np.argmin(plen)), 0, 100, 200, 255})
+    sub, sub_cu = parity.sub_layers([L2], inp.cu_prefix, blk, seqs)
+    s_idx, s_cu = oracle.compact(keep_ref[seqs])
+    ref = oracle.retained_attn(sub[0]["q"], sub[0]["k_blk"], sub[0]["v_blk"], s_idx, s_cu,
+                               sub[0]["k_cache"], sub[0]["v_cache"], sub_cu, blk, cfg.hq,
+                               cfg.hkv)
+    got = workloads.to_f32_numpy(ret)
+    got = np.concatenate([got[cu_h[b]:cu_h[b + 1]] for b in seqs])
+    err = parity.assert_close("retained (constrained set)", got, ref, parity.TOL["bf16"]["out"],
+                              parity.TIGHT["bf16"]["out"], rel_scale=True)
+    _record(dict(config=cfg.name, variants="paged 64-token pages == packed; layer 1 without O "
+                 "== with O; masked + both rules and dynamic budget == oracle on the GPU delta",
+                 sequences=n, retained_constrained_sequences_compared=len(seqs),
+                 retained_constrained_max_abs_err=float(f"{err:.3e}"), **counts))
+    del inp, step
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
 def test_c3_full_size_every_sequence():
     _full_size("c3", "c3", n_layers=3)
 
