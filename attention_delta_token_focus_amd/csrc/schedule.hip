@@ -17,7 +17,7 @@ namespace {
 // before sequence i; the four counts add up to its rank. Up to kMaxSort:
 // bitonic sort of (P_b, ~b) in LDS by 1024 threads. Larger batches keep
 // their natural order.
-constexpr int kMaxSort = 8192;
+constexpr int kMaxSort = 16384;  // 64-bit keys: 128 KiB of the 160 KiB of LDS
 constexpr int kRankMax = 256;
 
 __global__ void __launch_bounds__(1024) lpt_rank_kernel(

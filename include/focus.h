@@ -77,7 +77,7 @@ const char* focus_last_error(void);
  *              those sequences last.
  *  order       device int32 [batch] output, a permutation of 0..batch-1;
  *              nothing past order[batch-1] is written.
- * Batches above 8192 keep their natural order.
+ * Batches above 16384 keep their natural order.
  * Errors: INVALID_ARG (batch < 1, NULL pointer), HIP.
  */
 focus_status focus_schedule(int batch, const int32_t* cu_prefix, int32_t* order,

@@ -215,11 +215,11 @@ def test_rescale_path_hot_keys(name, over, plens, hot):
         assert torch.equal(imp, step.imp[0]) and torch.equal(lse, step.lse[0])
 
 
-@pytest.mark.parametrize("batch", [1, 7, 256, 257, 1000, 8192, 8193])
+@pytest.mark.parametrize("batch", [1, 7, 256, 257, 1000, 8193, 16384, 16385])
 def test_schedule_order(batch):
     """focus_schedule: longest prefix first, equal lengths by lower index
     (a stable sort on the negated lengths), on both sides of the 256-sequence
-    rank kernel / bitonic sort switch and of the 8192 limit past which the
+    rank kernel / bitonic sort switch and of the 16384 limit past which the
     natural order is kept. Lengths repeat often, to exercise the ties."""
     import attention_delta_token_focus_amd as F
     rng = np.random.default_rng(batch)
@@ -229,7 +229,7 @@ def test_schedule_order(batch):
     F.focus_schedule(batch, cu, order)
     torch.cuda.synchronize()
     got = order.cpu().numpy()
-    if batch > 8192:
+    if batch > 16384:
         want = np.arange(batch)
     else:
         want = np.argsort(-lens, kind="stable")
