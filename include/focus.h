@@ -29,7 +29,9 @@
  *    with round-to-nearest-even. Importances and lse are float32.
  *  - Supported shapes: 1 <= B <= 128, head_dim d in {64, 128}, Hq a
  *    multiple of Hkv. Query head h reads KV head h / (Hq / Hkv).
- *  - Calls are reentrant and thread-safe.
+ *  - Calls are reentrant and thread-safe, except that calls of
+ *    focus_block_attn_importance_noalloc that overlap in time on one GPU
+ *    share its static scratch and race.
  */
 #ifndef FOCUS_H_
 #define FOCUS_H_
