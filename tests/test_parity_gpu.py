@@ -94,6 +94,40 @@ def test_edge_cases(name, over, plens, kk):
     _case(name, cfg, n_layers=3, prefix_lens=plens, k_keep=kk)
 
 
+def _random_shapes(n=24, seed=7321):
+    """Seeded draws over the supported shapes (B 1..128, d 64 or 128, both
+    dtypes, G 1..16, odd pools up to 9), with prefix lengths near tile
+    edges and budgets from 0 to B, for combinations no list above names."""
+    rng = np.random.default_rng(seed)
+    near_edge = [0, 1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129]
+    cases = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        d = 128 if rng.random() < 0.7 else 64
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g * hkv <= 32]))
+        blk = int(rng.choice([int(rng.integers(1, 129)), int(rng.choice([1, 32, 64, 96, 128]))]))
+        pool = int(rng.choice([1, 3, 5, 7, 9]))
+        nseq = int(rng.integers(1, 5))
+        plens = [int(rng.choice(near_edge)) + 32 * int(rng.integers(0, 48))
+                 if rng.random() < 0.7 else int(rng.integers(0, 1600)) for _ in range(nseq)]
+        kk = [int(rng.integers(0, blk + 1)) for _ in range(nseq)]
+        over = dict(block=blk, hq=g * hkv, hkv=hkv, head_dim=d, dtype=dtype, pool_k=pool)
+        name = f"r{i} {dtype} d{d} B{blk} G{g} Hkv{hkv} k{pool} P{plens}"
+        cases.append((name, over, plens, kk))
+    return cases
+
+
+RANDOM = _random_shapes()
+
+
+@pytest.mark.parametrize("name,over,plens,kk", RANDOM, ids=[r[0].split()[0] for r in RANDOM])
+def test_random_shapes(name, over, plens, kk):
+    base = workloads.get("c2")
+    cfg = workloads.scaled(base, batch=len(plens), prefix_fixed=1, **over)
+    _case(name, cfg, n_layers=3, prefix_lens=plens, k_keep=kk)
+
+
 def test_retained_with_full_budget_equals_block_attention():
     """Cross-call pin: keeping every token, retained attention on layer L
     must reproduce block attention's output for layer L."""
