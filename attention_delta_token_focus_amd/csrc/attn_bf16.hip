@@ -65,12 +65,19 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// K/V rows are read once per launch (per head chunk): the direct-to-LDS
-// loads carry the non-temporal cache policy (nt); against the default
-// policy it measured 7% faster for block attention and 10% for retained
-// attention at B = 32, 3% slower at B = 128 (four head chunks per KV head
-// sharing L2).
-constexpr int kStreamPolicy = 2;  // cache-policy bits: nt
+// Cache policy of the direct-to-LDS K/V loads (POL, the instruction's
+// cache-policy bits). With one head chunk per KV head each K/V row is read
+// once per launch: nt (non-temporal), measured 7% faster for block and 10%
+// for retained attention at B = 32 than the default policy. With several
+// head chunks the chunks of an item stream the same rows close together on
+// one XCD and L2 serves the repeats: the default policy from three chunks
+// on, measured 3.6% faster for block attention at B = 128 (four chunks),
+// the launch after it 2-3% slower (what the cached rows leave in L2); at
+// B = 64 (two chunks) block attention gained nothing, so nt stays there.
+// Retained attention at these budgets has one chunk (its full-budget form
+// has the chunks of block attention).
+constexpr int kPolicyNt = 2;       // cache-policy bits: nt
+constexpr int kPolicyDefault = 0;
 
 // A wave-uniform pointer, moved to scalar registers explicitly.
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
@@ -85,12 +92,14 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
 }
+template <int POL>
 __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, kStreamPolicy);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, POL);
 }
 
+template <int POL>
 __device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, kStreamPolicy);
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, POL);
 }
 
 // 16 bytes of O to global memory with the sc1 and nt cache-policy bits (the
@@ -199,7 +208,7 @@ __device__ __forceinline__ bf16x8 cat8(u32x2v lo, u32x2v hi) {
 // CU, 8-stage ring), which halve the workgroups that stream the same K/V
 // when a KV head has more than 128 query rows, measured no faster at
 // B = 64 / 128 or G = 8.
-template <bool RET, int NBT, bool WO, bool PAGED>
+template <bool RET, int NBT, bool WO, bool PAGED, int POL>
 __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
     attn_bf16_kernel(const AttnArgs a) {
   constexpr int STAGEB = stage_bytes<WO>();
@@ -358,14 +367,14 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           char* dst = st + (SPW * wave + i) * 1024;
-          dma16b(rk, koff[i], dst);
+          dma16b<POL>(rk, koff[i], dst);
         }
         if constexpr (WO) {
           const auto rv = tile_rsrc(uniform_ptr(vc + tb));
 #pragma unroll
           for (int i = 0; i < SPW; ++i) {
             char* dst = st + (SPW * wave + i) * 1024;
-            dma16b(rv, voff[i], dst + TILEB);
+            dma16b<POL>(rv, voff[i], dst + TILEB);
           }
         }
         return;
@@ -378,8 +387,8 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
         // koff/voff hold lr * rowstride; take it back out in integers
         const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
         char* dst = st + (SPW * wave + i) * 1024;
-        dma16(kc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
-        if constexpr (WO) dma16(vc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
+        dma16<POL>(kc + (size_t)((ptrdiff_t)koff[i] + shift), dst);
+        if constexpr (WO) dma16<POL>(vc + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
       }
       return;
     }
@@ -398,8 +407,8 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
       }
       const ptrdiff_t shift = ((ptrdiff_t)row - lr) * (ptrdiff_t)rowstride;
       char* dst = st + (SPW * wave + i) * 1024;
-      dma16(kb + (size_t)((ptrdiff_t)koff[i] + shift), dst);
-      if constexpr (WO) dma16(vb + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
+      dma16<POL>(kb + (size_t)((ptrdiff_t)koff[i] + shift), dst);
+      if constexpr (WO) dma16<POL>(vb + (size_t)((ptrdiff_t)voff[i] + shift), dst + TILEB);
     }
   };
 
@@ -736,18 +745,18 @@ __global__ void __launch_bounds__(NW * 64, WO ? 2 : 3)
   }
 }
 
-template <bool RET, bool WO, bool PAGED>
+template <bool RET, bool WO, bool PAGED, int POL>
 hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(attn_grid_size(batch * a.Hkv, a.n_hc)), block(NW * 64);
   switch (nbt) {
     case 1:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 1, WO, PAGED, POL>), grid, block, 0, s, a);
       break;
     case 2:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 2, WO, PAGED, POL>), grid, block, 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<RET, 4, WO, PAGED, POL>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
@@ -755,8 +764,12 @@ hipError_t launch_nbt(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
 
 template <bool RET, bool WO>
 hipError_t launch_layout(int nbt, int batch, const AttnArgs& a, hipStream_t s) {
-  if (a.page_table != nullptr) return launch_nbt<RET, WO, true>(nbt, batch, a, s);
-  return launch_nbt<RET, WO, false>(nbt, batch, a, s);
+  if (a.n_hc >= 3) {
+    if (a.page_table != nullptr) return launch_nbt<RET, WO, true, kPolicyDefault>(nbt, batch, a, s);
+    return launch_nbt<RET, WO, false, kPolicyDefault>(nbt, batch, a, s);
+  }
+  if (a.page_table != nullptr) return launch_nbt<RET, WO, true, kPolicyNt>(nbt, batch, a, s);
+  return launch_nbt<RET, WO, false, kPolicyNt>(nbt, batch, a, s);
 }
 
 int block_tiles(int rows) {

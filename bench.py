@@ -381,12 +381,18 @@ def stream_read_reference(args, gib=4):
 
 def attn_kernel_name(cfg) -> str:
     """The block-attention kernel instantiation the workload runs: the
-    tuned bf16 d = 128 kernel with 1, 2 or 4 block tiles of 32 keys, else
-    the generic kernel."""
+    tuned bf16 d = 128 kernel with 1, 2 or 4 block tiles of 32 keys and the
+    K/V load cache policy the library picks (0, the default, from three
+    head chunks of up to 128 query rows per KV head on; 2, nt, below),
+    else the generic kernel."""
     if cfg.dtype != "bf16" or cfg.head_dim != 128:
         return "attn_kernel (generic)"
     nbt = 1 if cfg.block <= 32 else (2 if cfg.block <= 64 else 4)
-    return f"attn_bf16_kernel<false, {nbt}, true, false>"
+    g = cfg.hq // cfg.hkv
+    per = min(max(128 // cfg.block, 1), g)
+    n_hc = -(-g // per)
+    pol = 0 if n_hc >= 3 else 2
+    return f"attn_bf16_kernel<false, {nbt}, true, false, {pol}>"
 
 
 def main() -> int:
