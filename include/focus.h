@@ -16,7 +16,10 @@
  *  - Outputs must not alias inputs.
  *  - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
  *    default stream) and never synchronises. Device-side faults surface at
- *    the caller's next synchronisation.
+ *    the caller's next synchronisation. No call allocates, sets memory or
+ *    synchronises, so a sequence of calls on a capturing stream can be
+ *    recorded into a HIP graph (the workspace, when one is needed, must
+ *    then outlive the graph); replays give the same bits as the calls.
  *  - Device arrays (cu_prefix, k_keep, cu_ret, idx, keep) are never read on
  *    the host. Host integers documented as promises (max_prefix, n_ret,
  *    max_ret) must be true upper bounds / counts; the kernels clamp where

@@ -704,6 +704,70 @@ def test_masked_select_without_mask_or_rules_equals_focus_select():
     assert np.array_equal(idx.cpu().numpy()[:step.n_ret], r1["idx"])
 
 
+def _step_outputs(step):
+    """Every output of a step, the retained rows cut at the count the step
+    wrote (cu_ret[batch], read back after the step)."""
+    n = int(step.cu_ret[-1].item())
+    ts = [step.imp[0], step.imp[1], step.dI, step.keep, step.cu_ret, step.order,
+          step.idx[:n], step.ret_out[0][:n]]
+    ts += [o for o in step.out if o is not None]
+    ts += [x for x in step.lse if x is not None]
+    if step.cand is not None:
+        ts.append(step.cand)
+    return ts
+
+
+@pytest.mark.parametrize("masked_rules", [None, 3], ids=["plain", "masked-rules3"])
+def test_step_graph_replay_equals_eager(masked_rules):
+    """A whole block-step only enqueues work (no allocation, no memset, no
+    host synchronisation in any call), so it can be captured in a HIP
+    graph: every replay gives the same bits as the eager step, also with
+    eager steps run between the replays, including the masked selection
+    whose retained count is known only on the device."""
+    from attention_delta_token_focus_amd.step import FocusStep
+    cfg = workloads.scaled(workloads.get("c2"), batch=24)
+    log(f"[parity] graph replay of one block-step (masked rules {masked_rules})")
+    inp = workloads.make_inputs(cfg, 31, n_layers=3)
+    lay = parity.to_device(inp)
+    kw = {}
+    if masked_rules is not None:
+        kw = dict(masked=workloads.draw_masked(cfg, 31), rules=masked_rules)
+    step = FocusStep(parity.dims_of(cfg), inp.cu_prefix, inp.meta.k_keep, n_further=1,
+                     with_lse=True, **kw)
+    for _ in range(2):
+        step.run(lay)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in _step_outputs(step)]
+
+    def check():
+        got = _step_outputs(step)
+        assert len(got) == len(ref)
+        for a, b in zip(got, ref):
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        step.run(lay)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run(lay)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in _step_outputs(step):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check()
+        step.run(lay)
+        torch.cuda.synchronize()
+        check()
+
+
 def _paged_pool(kv, cu, page_size, seed, slack=3):
     """The same prefix rows scattered over shuffled pages of a NaN-filled
     pool (a wrong read shows up as NaN). Returns pool, page_table,
